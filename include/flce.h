@@ -1,0 +1,143 @@
+/*
+ * flce.h -- fused linear cross-entropy on AMD Instinct MI355X (gfx950).
+ *
+ * The operation ("Long-Sequence MoE RL Training: From First Principles to
+ * MI300X", section 3, Linear cross-entropy): for hidden states H [T x d] and
+ * an LM-head weight W [V x d], the logits are Z = H W^T [T x V].  Each token
+ * row is reduced to one cross-entropy value,
+ *     lse_i  = log sum_j exp(Z_ij)
+ *     loss_i = lse_i - Z_{i, y_i}          (= -log softmax(Z_i)[y_i]),
+ * and the backward needs only dZ = softmax(Z) - onehot(y), contracted into
+ *     dH = dZ W      and      dW = dZ^T H   (the page writes dW^T = H^T dZ).
+ * Z is never materialised: the forward streams vocabulary tiles through a
+ * running-max / log-sum-exp recurrence keeping O(block) scalars per token,
+ * and the backward recomputes each logit tile, forms its dZ tile and
+ * contracts it immediately, so vocab-axis residency is bounded by
+ * [token block x vocab slab] instead of [tokens x vocab] (same section; the
+ * Megatron-Lite / bumblebee write-up, section 2.3 step 1, streams along the
+ * vocab dimension in the same way).
+ *
+ * Conventions shared by every call:
+ *   - Matrices are row-major and dense: H[t*d + k], W[v*d + k], dH[t*d + k],
+ *     dW[v*d + k].  Element type of H, W and dH is the plan's dtype
+ *     (FLCE_BF16: bfloat16 bits, FLCE_F32: float); dW is always float.
+ *   - Targets y are int64 [T].  y_i == ignore_index marks an ignored token:
+ *     loss_i = 0 and its dZ row is zero (its lse is still computed).  A
+ *     target outside [0, V) that is not ignore_index is a precondition
+ *     violation: that token's loss, and the gradients it touches, are NaN.
+ *   - Every pointer argument except the host plan is device memory owned by
+ *     the caller.  The library never allocates device memory, never
+ *     synchronises the host, and keeps no state between calls other than a
+ *     thread-local error string.  All work is ordered on `stream` (a
+ *     hipStream_t; NULL means the default stream).
+ *   - Requirements: T >= 0, V >= 1, d >= 8 and d % 8 == 0, T, V < 2^31,
+ *     d <= 65536, device pointers 16-byte aligned.  Violations are reported
+ *     before anything is launched.
+ *   - Results are bitwise reproducible for identical inputs and plan: every
+ *     reduction runs in a fixed order, and no floating-point atomics are used.
+ *   - Errors are returned as flce_status_t; nothing throws across the ABI.
+ */
+#ifndef FLCE_H_
+#define FLCE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum flce_dtype { FLCE_F32 = 0, FLCE_BF16 = 1 } flce_dtype_t;
+
+typedef enum flce_status {
+  FLCE_OK = 0,
+  FLCE_ERR_INVALID_ARG = -1, /* null pointer, bad size, bad plan */
+  FLCE_ERR_UNSUPPORTED = -2, /* shape or alignment outside the requirements */
+  FLCE_ERR_WORKSPACE = -3,   /* workspace too small, or cap below the minimum */
+  FLCE_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+} flce_status_t;
+
+/* A launch plan.  Plain data: produced on the host by flce_plan(), read by
+ * flce_forward()/flce_backward(); it may be copied freely. */
+typedef struct flce_plan {
+  int64_t T, d, V;
+  int32_t dtype;          /* flce_dtype_t */
+  int32_t elem_bytes;     /* 2 (bf16) or 4 (f32) */
+  /* forward: tiles of tile_v vocab rows x tile_t tokens; the vocab axis is
+   * cut into fwd_splits contiguous ranges reduced independently and merged */
+  int32_t tile_v, tile_t;
+  int32_t fwd_splits;
+  int32_t fwd_tiles_per_split; /* vocab tiles in each split */
+  /* backward: token blocks of bwd_block tokens x vocab slabs of bwd_slab */
+  int64_t bwd_block, bwd_slab;
+  int64_t n_blocks, n_slabs;
+  /* workspace (bytes); one buffer of ws_bytes serves both calls */
+  uint64_t fwd_ws_bytes;   /* per-split (max, sum) partials + target logits */
+  uint64_t dz_ws_bytes;    /* the [bwd_block x bwd_slab] dZ tile buffer */
+  uint64_t dh_acc_bytes;   /* fp32 dH accumulator, 0 when there is one slab */
+  uint64_t bwd_ws_bytes;   /* dz_ws_bytes + dh_acc_bytes */
+  uint64_t ws_bytes;       /* max(fwd_ws_bytes, bwd_ws_bytes) */
+  uint64_t vocab_ws_cap;   /* the cap the planner honoured */
+  /* context: bytes of one materialised [T x V] logits copy in the dtype */
+  uint64_t naive_logits_bytes;
+  uint32_t magic;          /* set by flce_plan; checked by the other calls */
+  uint32_t reserved;
+} flce_plan_t;
+
+/* flce_plan -- choose tiles, splits, token block and vocab slab.
+ *   T, d, V : problem size (see requirements above).
+ *   dtype   : element type of H, W, dH.
+ *   vocab_ws_cap_bytes : upper bound for the backward workspace (the dZ
+ *             buffer plus the fp32 dH accumulator); 0 selects the default of
+ *             950,000,000 bytes, keeping vocab-axis residency below 1 GB.
+ *             Caps above 2^31 - 65536 bytes are lowered to that value.
+ *   out     : host pointer, filled on success.
+ * Host-only integer arithmetic; launches nothing.  Returns
+ * FLCE_ERR_INVALID_ARG for a null `out`, negative/zero sizes or an unknown
+ * dtype, FLCE_ERR_UNSUPPORTED for d % 8 != 0 or sizes beyond the limits, and
+ * FLCE_ERR_WORKSPACE when the cap cannot hold the smallest token block. */
+flce_status_t flce_plan(int64_t T, int64_t d, int64_t V, flce_dtype_t dtype,
+                        uint64_t vocab_ws_cap_bytes, flce_plan_t* out);
+
+/* flce_forward -- per-token loss and lse (section 3 of the first page).
+ *   H [T x d], W [V x d] in the plan's dtype; y [T] int64.
+ *   scale   : multiplies the optional reduced loss only (1/N gives a mean).
+ *   loss [T], lse [T] : float outputs; loss is the unscaled per-token value.
+ *   loss_reduced : NULL, or a device float that receives scale * sum(loss)
+ *             (summed in a fixed order, in double precision).
+ *   ws, ws_bytes : caller workspace of at least plan->fwd_ws_bytes.
+ * T == 0 is valid and writes only loss_reduced (= 0). */
+flce_status_t flce_forward(const flce_plan_t* plan, const void* H, const void* W,
+                           const int64_t* y, int64_t ignore_index, float scale, float* loss,
+                           float* lse, float* loss_reduced, void* ws, uint64_t ws_bytes,
+                           void* stream);
+
+/* flce_backward -- dH and dW of grad_scale * sum_i loss_i.
+ *   lse [T]  : the forward's output for the same H, W (its normaliser lets
+ *              the recompute form softmax without a running max).
+ *   grad_scale : scalar multiplying every dZ element (1/N for a mean).
+ *   dH [T x d] : output in the plan's dtype (fp32 accumulation, rounded to
+ *              nearest even once at the end for bf16).
+ *   dW [V x d] : float; overwritten, or accumulated into when
+ *              accumulate_dW != 0 (gradient accumulation across calls).
+ *   ws, ws_bytes : caller workspace of at least plan->bwd_ws_bytes.
+ * T == 0 is valid: dW is zeroed (or left as is when accumulating). */
+flce_status_t flce_backward(const flce_plan_t* plan, const void* H, const void* W,
+                            const int64_t* y, const float* lse, int64_t ignore_index,
+                            float grad_scale, void* dH, float* dW, int accumulate_dW, void* ws,
+                            uint64_t ws_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* flce_status_string(flce_status_t status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* flce_last_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char* flce_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLCE_H_ */

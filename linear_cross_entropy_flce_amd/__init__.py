@@ -1,0 +1,14 @@
+"""Fused linear cross-entropy for AMD Instinct MI355X (gfx950).
+
+The computation runs in hand-written HIP kernels in libflce.so, reached
+through the C-ABI declared in include/flce.h; this package only marshals
+arguments (torch supplies device memory and the stream).
+"""
+from ._lib import (EXPORTED, FLCE_BF16, FLCE_ERR_HIP, FLCE_ERR_INVALID_ARG, FLCE_ERR_UNSUPPORTED,
+                   FLCE_ERR_WORKSPACE, FLCE_F32, FLCE_OK, FlceError, Plan, flce_backward,
+                   flce_forward, flce_plan, flce_plan_status, last_error, load, version, workspace)
+
+__all__ = ["EXPORTED", "FLCE_BF16", "FLCE_ERR_HIP", "FLCE_ERR_INVALID_ARG", "FLCE_ERR_UNSUPPORTED",
+           "FLCE_ERR_WORKSPACE", "FLCE_F32", "FLCE_OK", "FlceError", "Plan", "flce_backward",
+           "flce_forward", "flce_plan", "flce_plan_status", "last_error", "load", "version",
+           "workspace"]

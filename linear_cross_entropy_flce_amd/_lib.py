@@ -1,0 +1,220 @@
+"""ctypes binding of libflce.so: argument marshalling only.
+
+Every entry point mirrors the C-ABI of include/flce.h under the same name.
+Torch tensors are accepted for device buffers; only their data pointers,
+shapes and the current HIP stream are passed on.  No arithmetic of the method
+happens here, and there is no fallback: if the library is missing or a call
+fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("FLCE_LIB", os.path.join(PKG, "libflce.so"))
+
+FLCE_F32 = 0
+FLCE_BF16 = 1
+FLCE_OK = 0
+FLCE_ERR_INVALID_ARG = -1
+FLCE_ERR_UNSUPPORTED = -2
+FLCE_ERR_WORKSPACE = -3
+FLCE_ERR_HIP = -4
+
+EXPORTED = ["flce_plan", "flce_forward", "flce_backward", "flce_status_string",
+            "flce_last_error", "flce_version"]
+
+
+class Plan(ctypes.Structure):
+    """Mirror of flce_plan_t."""
+    _fields_ = [
+        ("T", ctypes.c_int64), ("d", ctypes.c_int64), ("V", ctypes.c_int64),
+        ("dtype", ctypes.c_int32), ("elem_bytes", ctypes.c_int32),
+        ("tile_v", ctypes.c_int32), ("tile_t", ctypes.c_int32),
+        ("fwd_splits", ctypes.c_int32), ("fwd_tiles_per_split", ctypes.c_int32),
+        ("bwd_block", ctypes.c_int64), ("bwd_slab", ctypes.c_int64),
+        ("n_blocks", ctypes.c_int64), ("n_slabs", ctypes.c_int64),
+        ("fwd_ws_bytes", ctypes.c_uint64), ("dz_ws_bytes", ctypes.c_uint64),
+        ("dh_acc_bytes", ctypes.c_uint64), ("bwd_ws_bytes", ctypes.c_uint64),
+        ("ws_bytes", ctypes.c_uint64), ("vocab_ws_cap", ctypes.c_uint64),
+        ("naive_logits_bytes", ctypes.c_uint64),
+        ("magic", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+    ]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class FlceError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"flce status {status}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Loads libflce.so (once).  Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m linear_cross_entropy_flce_amd.build` "
+                          "(or __graft_entry__.build()) first -- there is no fallback path")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(Plan)
+    vp, i64, f32, u64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_uint64
+    lib.flce_plan.argtypes = [i64, i64, i64, ctypes.c_int, u64, P]
+    lib.flce_plan.restype = ctypes.c_int
+    lib.flce_forward.argtypes = [P, vp, vp, vp, i64, f32, vp, vp, vp, vp, u64, vp]
+    lib.flce_forward.restype = ctypes.c_int
+    lib.flce_backward.argtypes = [P, vp, vp, vp, vp, i64, f32, vp, vp, ctypes.c_int, vp, u64, vp]
+    lib.flce_backward.restype = ctypes.c_int
+    lib.flce_status_string.argtypes = [ctypes.c_int]
+    lib.flce_status_string.restype = ctypes.c_char_p
+    lib.flce_last_error.argtypes = []
+    lib.flce_last_error.restype = ctypes.c_char_p
+    lib.flce_version.argtypes = []
+    lib.flce_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != FLCE_OK:
+        lib = load()
+        raise FlceError(status, lib.flce_status_string(status).decode() + ": " +
+                        lib.flce_last_error().decode())
+
+
+def last_error() -> str:
+    return load().flce_last_error().decode()
+
+
+def version() -> str:
+    return load().flce_version().decode()
+
+
+# ------------------------------------------------------------ marshalling
+
+def _ptr(x) -> int | None:
+    """Device pointer of a tensor, an int pointer, or None (NULL)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dtype_code(dtype) -> int:
+    import torch
+    if dtype in (torch.bfloat16, "bf16", FLCE_BF16):
+        return FLCE_BF16
+    if dtype in (torch.float32, "f32", FLCE_F32):
+        return FLCE_F32
+    raise ValueError(f"unsupported dtype {dtype}")
+
+
+def flce_plan(T: int, d: int, V: int, dtype, vocab_ws_cap_bytes: int = 0) -> Plan:
+    """flce_plan(): host-only planning.  dtype: torch dtype, 'bf16'/'f32' or code."""
+    code = _dtype_code(dtype) if not isinstance(dtype, int) or dtype in (0, 1) else dtype
+    p = Plan()
+    _check(load().flce_plan(int(T), int(d), int(V), int(code), int(vocab_ws_cap_bytes),
+                            ctypes.byref(p)))
+    return p
+
+
+def flce_plan_status(T, d, V, dtype_code: int, cap: int = 0):
+    """Raw status of flce_plan (for tests of the error paths)."""
+    p = Plan()
+    st = load().flce_plan(int(T), int(d), int(V), int(dtype_code), int(cap), ctypes.byref(p))
+    return st, p
+
+
+def workspace(plan: Plan, device="cuda"):
+    """A caller-owned workspace of plan.ws_bytes (torch uint8 tensor)."""
+    import torch
+    return torch.empty(max(int(plan.ws_bytes), 16), dtype=torch.uint8, device=device)
+
+
+def _check_tensor(name, t, shape, dtype):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def _elem_dtype(plan: Plan):
+    import torch
+    return torch.bfloat16 if plan.dtype == FLCE_BF16 else torch.float32
+
+
+def flce_forward(plan: Plan, H, W, y, ignore_index: int = -100, scale: float = 1.0, loss=None,
+                 lse=None, loss_reduced=None, ws=None, stream=None):
+    """flce_forward(): returns (loss, lse, loss_reduced or None) as tensors.
+
+    Outputs not given are allocated with torch on W's device."""
+    import torch
+    T, d, V = plan.T, plan.d, plan.V
+    dev = W.device
+    et = _elem_dtype(plan)
+    _check_tensor("H", H, (T, d), et)
+    _check_tensor("W", W, (V, d), et)
+    _check_tensor("y", y, (T,), torch.int64)
+    if loss is None:
+        loss = torch.empty(T, dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(T, dtype=torch.float32, device=dev)
+    _check_tensor("loss", loss, (T,), torch.float32)
+    _check_tensor("lse", lse, (T,), torch.float32)
+    if ws is None:
+        ws = workspace(plan, dev)
+    _check(load().flce_forward(ctypes.byref(plan), _ptr(H), _ptr(W), _ptr(y), int(ignore_index),
+                               float(scale), _ptr(loss), _ptr(lse), _ptr(loss_reduced), _ptr(ws),
+                               int(ws.numel() * ws.element_size()), _stream(stream)))
+    return loss, lse, loss_reduced
+
+
+def flce_backward(plan: Plan, H, W, y, lse, ignore_index: int = -100, grad_scale: float = 1.0,
+                  dH=None, dW=None, accumulate_dW: bool = False, ws=None, stream=None):
+    """flce_backward(): returns (dH, dW).  dW is float32 [V, d]."""
+    import torch
+    T, d, V = plan.T, plan.d, plan.V
+    dev = W.device
+    et = _elem_dtype(plan)
+    _check_tensor("H", H, (T, d), et)
+    _check_tensor("W", W, (V, d), et)
+    _check_tensor("y", y, (T,), torch.int64)
+    _check_tensor("lse", lse, (T,), torch.float32)
+    if dH is None:
+        dH = torch.empty((T, d), dtype=et, device=dev)
+    if dW is None:
+        if accumulate_dW:
+            raise ValueError("accumulate_dW needs an existing dW")
+        dW = torch.empty((V, d), dtype=torch.float32, device=dev)
+    _check_tensor("dH", dH, (T, d), et)
+    _check_tensor("dW", dW, (V, d), torch.float32)
+    if ws is None:
+        ws = workspace(plan, dev)
+    _check(load().flce_backward(ctypes.byref(plan), _ptr(H), _ptr(W), _ptr(y), _ptr(lse),
+                                int(ignore_index), float(grad_scale), _ptr(dH), _ptr(dW),
+                                1 if accumulate_dW else 0, _ptr(ws),
+                                int(ws.numel() * ws.element_size()), _stream(stream)))
+    return dH, dW

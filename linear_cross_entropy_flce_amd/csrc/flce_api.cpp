@@ -1,0 +1,324 @@
+// flce_api.cpp -- the C-ABI: planning, argument validation and launch order.
+//
+// Host-only code.  Nothing here allocates device memory or synchronises; every
+// launch goes to the caller's stream in a fixed order, so results are
+// reproducible bit for bit.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/flce.h"
+#include "flce_launch.h"
+
+namespace {
+
+constexpr uint32_t kPlanMagic = 0x464c4345u;  // "FLCE"
+constexpr uint64_t kDefaultCap = 950000000ull;
+constexpr uint64_t kMaxCap = 0x7fff0000ull;
+constexpr int64_t kMaxBlock = 8192;
+constexpr int kTargetWorkgroups = 256;  // one per compute unit
+
+thread_local char g_err[512] = "";
+
+flce_status_t fail(flce_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+flce_status_t ok() {
+  g_err[0] = 0;
+  return FLCE_OK;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+flce_status_t check_plan(const flce_plan_t* p) {
+  if (!p) return fail(FLCE_ERR_INVALID_ARG, "plan is NULL");
+  if (p->magic != kPlanMagic) return fail(FLCE_ERR_INVALID_ARG, "plan was not made by flce_plan");
+  return FLCE_OK;
+}
+
+flce_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(FLCE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* flce_version(void) { return "0.1.0"; }
+
+const char* flce_last_error(void) { return g_err; }
+
+const char* flce_status_string(flce_status_t s) {
+  switch (s) {
+    case FLCE_OK: return "ok";
+    case FLCE_ERR_INVALID_ARG: return "invalid argument";
+    case FLCE_ERR_UNSUPPORTED: return "unsupported shape or alignment";
+    case FLCE_ERR_WORKSPACE: return "workspace too small";
+    case FLCE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+flce_status_t flce_plan(int64_t T, int64_t d, int64_t V, flce_dtype_t dtype, uint64_t cap,
+                        flce_plan_t* out) {
+  if (!out) return fail(FLCE_ERR_INVALID_ARG, "out is NULL");
+  if (dtype != FLCE_F32 && dtype != FLCE_BF16)
+    return fail(FLCE_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (T < 0) return fail(FLCE_ERR_INVALID_ARG, "T = %lld < 0", (long long)T);
+  if (d <= 0) return fail(FLCE_ERR_INVALID_ARG, "d = %lld <= 0", (long long)d);
+  if (V <= 0) return fail(FLCE_ERR_INVALID_ARG, "V = %lld <= 0", (long long)V);
+  if (d % 8 != 0) return fail(FLCE_ERR_UNSUPPORTED, "d = %lld is not a multiple of 8", (long long)d);
+  if (d > 65536) return fail(FLCE_ERR_UNSUPPORTED, "d = %lld > 65536", (long long)d);
+  if (T >= (1ll << 31) || V >= (1ll << 31))
+    return fail(FLCE_ERR_UNSUPPORTED, "T and V must be below 2^31");
+
+  const bool bf16 = dtype == FLCE_BF16;
+  const int64_t esz = bf16 ? 2 : 4;
+  const flce::TileInfo ti = flce::tile_info(bf16);
+  if (cap == 0) cap = kDefaultCap;
+  // tile offsets into the workspace are 32-bit: keep it below 2 GiB
+  if (cap > kMaxCap) cap = kMaxCap;
+
+  flce_plan_t p;
+  memset(&p, 0, sizeof p);
+  p.T = T;
+  p.d = d;
+  p.V = V;
+  p.dtype = (int32_t)dtype;
+  p.elem_bytes = (int32_t)esz;
+  p.tile_v = ti.logit_bm;
+  p.tile_t = ti.logit_bn;
+
+  // ---- forward: split the vocab tiles so that there are at least
+  // kTargetWorkgroups workgroups, and at least 8 splits for L2 sharing.
+  const int64_t n_tt = cdiv(T, ti.logit_bn);
+  const int64_t n_vt = cdiv(V, ti.logit_bm);
+  int64_t splits = cdiv(kTargetWorkgroups, n_tt > 0 ? n_tt : 1);
+  if (splits < 8) splits = 8;
+  if (splits > n_vt) splits = n_vt;
+  const int64_t tps = cdiv(n_vt, splits);
+  splits = cdiv(n_vt, tps);
+  p.fwd_splits = (int32_t)splits;
+  p.fwd_tiles_per_split = (int32_t)tps;
+  p.fwd_ws_bytes = (uint64_t)round_up(splits * T * 2 * 4, 256) + (uint64_t)round_up(T * 4, 256);
+
+  // ---- backward: largest token block (<= 8192, tile multiple) whose dZ
+  // buffer (plus fp32 dH accumulator when the vocab needs several slabs)
+  // fits under the cap.
+  const int64_t Tr = round_up(T > 0 ? T : 1, ti.logit_bn);
+  const int64_t Vfull = round_up(V, ti.logit_bm);
+  int64_t best_B = 0, best_Vs = 0, best_slabs = 0;
+  for (int64_t B = (Tr < kMaxBlock ? Tr : kMaxBlock); B >= ti.logit_bn; B -= ti.logit_bn) {
+    if ((uint64_t)(B * Vfull * esz) <= cap) {
+      best_B = B;
+      best_Vs = Vfull;
+      best_slabs = 1;
+      break;
+    }
+    const int64_t acc = B * d * 4;
+    if ((uint64_t)acc >= cap) continue;
+    const int64_t avail = (int64_t)cap - acc;
+    const int64_t vs_max = (avail / (B * esz)) / ti.logit_bm * ti.logit_bm;
+    if (vs_max < ti.logit_bm) continue;
+    const int64_t slabs = cdiv(Vfull, vs_max);
+    best_B = B;
+    best_Vs = round_up(cdiv(Vfull, slabs), ti.logit_bm);
+    best_slabs = cdiv(V, best_Vs);
+    break;
+  }
+  if (best_B == 0)
+    return fail(FLCE_ERR_WORKSPACE,
+                "cap of %llu bytes cannot hold the smallest %d-token block x %d-vocab slab",
+                (unsigned long long)cap, ti.logit_bn, ti.logit_bm);
+  p.bwd_block = best_B;
+  p.bwd_slab = best_Vs;
+  p.n_blocks = T > 0 ? cdiv(T, best_B) : 0;
+  p.n_slabs = best_slabs;
+  p.dz_ws_bytes = (uint64_t)(best_B * best_Vs * esz);
+  p.dh_acc_bytes = best_slabs > 1 ? (uint64_t)(best_B * d * 4) : 0;
+  p.bwd_ws_bytes = p.dz_ws_bytes + p.dh_acc_bytes;
+  p.ws_bytes = p.fwd_ws_bytes > p.bwd_ws_bytes ? p.fwd_ws_bytes : p.bwd_ws_bytes;
+  p.vocab_ws_cap = cap;
+  p.naive_logits_bytes = (uint64_t)T * (uint64_t)V * (uint64_t)esz;
+  p.magic = kPlanMagic;
+  *out = p;
+  return ok();
+}
+
+flce_status_t flce_forward(const flce_plan_t* plan, const void* H, const void* W, const int64_t* y,
+                           int64_t ignore_index, float scale, float* loss, float* lse,
+                           float* loss_reduced, void* ws, uint64_t ws_bytes, void* stream) {
+  flce_status_t st = check_plan(plan);
+  if (st != FLCE_OK) return st;
+  const flce_plan_t& p = *plan;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (!W) return fail(FLCE_ERR_INVALID_ARG, "W is NULL");
+  if (p.T > 0 && (!H || !y || !loss || !lse || !ws))
+    return fail(FLCE_ERR_INVALID_ARG, "H, y, loss, lse and ws must be non-NULL when T > 0");
+  if (misaligned(H) || misaligned(W) || misaligned(ws))
+    return fail(FLCE_ERR_UNSUPPORTED, "H, W and ws must be 16-byte aligned");
+  if (p.T > 0 && ws_bytes < p.fwd_ws_bytes)
+    return fail(FLCE_ERR_WORKSPACE, "forward needs %llu workspace bytes, got %llu",
+                (unsigned long long)p.fwd_ws_bytes, (unsigned long long)ws_bytes);
+  const bool bf16 = p.dtype == FLCE_BF16;
+  hipError_t e;
+  if (p.T == 0) {
+    if (loss_reduced) {
+      e = flce::launch_loss_sum(loss, 0, scale, loss_reduced, s);
+      if (e != hipSuccess) return hip_fail(e, "loss_sum launch");
+    }
+    return ok();
+  }
+  float* part = reinterpret_cast<float*>(ws);
+  float* zt = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
+                                       round_up((int64_t)p.fwd_splits * p.T * 2 * 4, 256));
+  flce::FwdArgs a;
+  a.H = H;
+  a.W = W;
+  a.y = y;
+  a.ignore_index = ignore_index;
+  a.T = p.T;
+  a.d = (int)p.d;
+  a.V = (int)p.V;
+  a.n_ttiles = (int)cdiv(p.T, p.tile_t);
+  a.n_vtiles = (int)cdiv(p.V, p.tile_v);
+  a.splits = p.fwd_splits;
+  a.tps = p.fwd_tiles_per_split;
+  a.grp = p.fwd_splits >= 32 ? 1 : 32 / p.fwd_splits;
+  a.part = part;
+  a.zt = zt;
+  const int64_t per_group = (int64_t)a.grp * a.splits;
+  const int64_t groups = cdiv(a.n_ttiles, a.grp);
+  const int64_t grid = 8 * per_group * cdiv(groups, 8);
+  e = flce::launch_fwd_sweep(a, bf16, (int)grid, s);
+  if (e != hipSuccess) return hip_fail(e, "forward sweep launch");
+  flce::MergeArgs m;
+  m.part = part;
+  m.zt = zt;
+  m.y = y;
+  m.ignore_index = ignore_index;
+  m.T = p.T;
+  m.V = (int)p.V;
+  m.splits = p.fwd_splits;
+  m.loss = loss;
+  m.lse = lse;
+  e = flce::launch_fwd_merge(m, s);
+  if (e != hipSuccess) return hip_fail(e, "forward merge launch");
+  if (loss_reduced) {
+    e = flce::launch_loss_sum(loss, p.T, scale, loss_reduced, s);
+    if (e != hipSuccess) return hip_fail(e, "loss_sum launch");
+  }
+  return ok();
+}
+
+flce_status_t flce_backward(const flce_plan_t* plan, const void* H, const void* W, const int64_t* y,
+                            const float* lse, int64_t ignore_index, float grad_scale, void* dH,
+                            float* dW, int accumulate_dW, void* ws, uint64_t ws_bytes,
+                            void* stream) {
+  flce_status_t st = check_plan(plan);
+  if (st != FLCE_OK) return st;
+  const flce_plan_t& p = *plan;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (!W || !dW) return fail(FLCE_ERR_INVALID_ARG, "W and dW must be non-NULL");
+  if (p.T > 0 && (!H || !y || !lse || !dH || !ws))
+    return fail(FLCE_ERR_INVALID_ARG, "H, y, lse, dH and ws must be non-NULL when T > 0");
+  if (misaligned(H) || misaligned(W) || misaligned(dH) || misaligned(dW) || misaligned(ws))
+    return fail(FLCE_ERR_UNSUPPORTED, "H, W, dH, dW and ws must be 16-byte aligned");
+  if (p.T > 0 && ws_bytes < p.bwd_ws_bytes)
+    return fail(FLCE_ERR_WORKSPACE, "backward needs %llu workspace bytes, got %llu",
+                (unsigned long long)p.bwd_ws_bytes, (unsigned long long)ws_bytes);
+  const bool bf16 = p.dtype == FLCE_BF16;
+  const flce::TileInfo ti = flce::tile_info(bf16);
+  hipError_t e;
+  if (p.T == 0) {
+    if (!accumulate_dW) {
+      e = flce::launch_fill_zero(dW, p.V * p.d, s);
+      if (e != hipSuccess) return hip_fail(e, "dW fill launch");
+    }
+    return ok();
+  }
+  void* dz = ws;
+  float* dh_acc = p.dh_acc_bytes ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
+                                                            p.dz_ws_bytes)
+                                 : nullptr;
+  for (int64_t b = 0; b < p.n_blocks; ++b) {
+    const int64_t t_begin = b * p.bwd_block;
+    const int t_count = (int)(p.T - t_begin < p.bwd_block ? p.T - t_begin : p.bwd_block);
+    for (int64_t sl = 0; sl < p.n_slabs; ++sl) {
+      const int64_t v_begin = sl * p.bwd_slab;
+      const int v_count = (int)(p.V - v_begin < p.bwd_slab ? p.V - v_begin : p.bwd_slab);
+
+      flce::DzArgs z;
+      z.H = H;
+      z.W = W;
+      z.y = y;
+      z.lse = lse;
+      z.ignore_index = ignore_index;
+      z.T = p.T;
+      z.d = (int)p.d;
+      z.V = (int)p.V;
+      z.t_begin = t_begin;
+      z.t_count = t_count;
+      z.v_begin = v_begin;
+      z.n_vtiles = (int)cdiv(v_count, ti.logit_bm);
+      z.n_ttiles = (int)cdiv(t_count, ti.logit_bn);
+      z.ldz = p.bwd_slab;
+      z.ldz_cols = (int64_t)z.n_vtiles * ti.logit_bm;
+      z.grad_scale = grad_scale;
+      z.dz = dz;
+      e = flce::launch_bwd_dz(z, bf16, s);
+      if (e != hipSuccess) return hip_fail(e, "dZ launch");
+
+      flce::DhArgs h;
+      h.dz = dz;
+      h.W = W;
+      h.ldz = p.bwd_slab;
+      h.d = (int)p.d;
+      h.V = (int)p.V;
+      h.t_begin = t_begin;
+      h.t_count = t_count;
+      h.v_begin = v_begin;
+      h.k_count = v_count;
+      h.n_mtiles = (int)cdiv(t_count, ti.dh_bm);
+      h.n_ntiles = (int)cdiv(p.d, ti.dh_bn);
+      if (p.n_slabs == 1) h.mode = 3;
+      else if (sl == 0) h.mode = 0;
+      else if (sl + 1 < p.n_slabs) h.mode = 1;
+      else h.mode = 2;
+      h.dh_acc = dh_acc;
+      h.dH = dH;
+      e = flce::launch_bwd_dh(h, bf16, s);
+      if (e != hipSuccess) return hip_fail(e, "dH launch");
+
+      flce::DwArgs w;
+      w.dz = dz;
+      w.H = H;
+      w.ldz = p.bwd_slab;
+      w.T = p.T;
+      w.d = (int)p.d;
+      w.t_begin = t_begin;
+      w.t_count = t_count;
+      w.v_begin = v_begin;
+      w.v_count = v_count;
+      w.n_mtiles = (int)cdiv(v_count, ti.dw_bm);
+      w.n_ntiles = (int)cdiv(p.d, ti.dw_bn);
+      w.accumulate = (b > 0 || accumulate_dW) ? 1 : 0;
+      w.dW = dW;
+      e = flce::launch_bwd_dw(w, bf16, s);
+      if (e != hipSuccess) return hip_fail(e, "dW launch");
+    }
+  }
+  return ok();
+}
+
+}  // extern "C"

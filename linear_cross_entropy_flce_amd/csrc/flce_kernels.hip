@@ -1,0 +1,581 @@
+// flce_kernels.hip -- the fused linear cross-entropy kernels for gfx950.
+//
+// Orientation: every logit tile is computed transposed, Z^T = W H^T, with the
+// vocab axis as the MFMA M dimension and tokens as N.  A lane then holds 16
+// vocab rows of one token column per 32x32 block, so the per-token softmax
+// statistics reduce inside the lane's own registers; the two half-waves
+// (rows 4*(lane/32)..) and the waves stacked along M are merged only once, at
+// the end of a workgroup's sweep.
+//
+// Kernels (the method is section 3 of "Long-Sequence MoE RL Training: From
+// First Principles to MI300X"):
+//   fwd_sweep   logits tile + running max / log-sum-exp over the workgroup's
+//               vocab range, target logit captured from the fp32 accumulator;
+//               writes per-split (max, sum) partials and z_target.
+//   fwd_merge   merges the splits in ascending order: lse, loss.
+//   loss_sum    fixed-order double-precision sum for the reduced loss.
+//   bwd_dz      recomputed logits tile -> dZ = g * (exp(z - lse) - onehot),
+//               stored (bf16 or fp32) to the [block x slab] workspace.
+//   bwd_dh      dH_block (+)= dZ W_slab   (fp32 accumulate, cast at the end).
+//   bwd_dw      dW_slab (+)= dZ^T H_block (fp32, deterministic block order).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "flce_launch.h"
+#include "flce_tile.hpp"
+
+namespace flce {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Logits tiles: 256 vocab x 256 tokens, 2 x 4 waves of 128 x 64 (bf16);
+// 128 x 128 with 2 x 2 waves of 64 x 64 for fp32.
+template <typename E>
+struct LogitCfg;
+template <>
+struct LogitCfg<__bf16> {
+  using T = Tile<256, 256, 2, 4, __bf16, true, true>;
+};
+template <>
+struct LogitCfg<float> {
+  using T = Tile<128, 128, 2, 2, float, true, true>;
+};
+
+// Contraction tiles for dH (A = dZ K-contiguous, B = W MN-contiguous) and dW
+// (A = dZ MN-contiguous, B = H MN-contiguous).
+template <typename E>
+struct DhCfg;
+template <>
+struct DhCfg<__bf16> {
+  using T = Tile<256, 256, 2, 4, __bf16, true, false>;
+};
+template <>
+struct DhCfg<float> {
+  using T = Tile<128, 128, 2, 2, float, true, false>;
+};
+template <typename E>
+struct DwCfg;
+template <>
+struct DwCfg<__bf16> {
+  using T = Tile<256, 256, 2, 4, __bf16, false, false>;
+};
+template <>
+struct DwCfg<float> {
+  using T = Tile<128, 128, 2, 2, float, false, false>;
+};
+
+__device__ __forceinline__ uint32_t clamp_bytes(int64_t b) {
+  return (uint32_t)(b < 0 ? 0 : (b > 0x7fffffffLL ? 0x7fffffffLL : b));
+}
+
+// Target of token t as an int in [0, V), or -1 when ignored, -2 when invalid.
+__device__ __forceinline__ int target_code(const int64_t* y, int64_t t, int64_t ignore, int V) {
+  const int64_t v = y[t];
+  if (v == ignore) return -1;
+  if (v < 0 || v >= V) return -2;
+  return (int)v;
+}
+
+// ============================================================== forward sweep
+//
+// Workgroup (token tile tt, split s) sweeps vocab tiles
+// [s * tps, min((s+1) * tps, n_vtiles)).  The linear workgroup id is mapped so
+// that the 32 workgroups an XCD holds at once are `grp` token tiles x `spl`
+// splits: they share H panels within a token tile and W panels across the
+// token tiles, in that XCD's L2.
+template <typename E>
+__global__ void __launch_bounds__(LogitCfg<E>::T::NT, 1)
+    fwd_sweep_kernel(FwdArgs a) {
+  using TL = typename LogitCfg<E>::T;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  constexpr int ESZ = TL::ESZ;
+
+  // ---- workgroup -> (token tile, split)
+  const int bid = blockIdx.x;
+  const int x = bid & 7, q = bid >> 3;
+  const int per_group = a.grp * a.splits;
+  const int gi = (q / per_group) * 8 + x;
+  const int within = q % per_group;
+  const int split = within / a.grp;
+  const int tt = gi * a.grp + within % a.grp;
+  if (tt >= a.n_ttiles) return;
+  const int vt_begin = split * a.tps;
+  const int vt_end = min(vt_begin + a.tps, a.n_vtiles);
+  if (vt_begin >= vt_end) return;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave / TL::WN, wn = wave % TL::WN;
+  const int64_t t0 = (int64_t)tt * TL::BN;
+
+  // B operand: H rows of this token tile (K-contiguous).
+  Operand B;
+  B.base = reinterpret_cast<const char*>(a.H) + t0 * a.d * ESZ;
+  B.ld_bytes = (uint32_t)(a.d * ESZ);
+  B.rows = (int)min<int64_t>(TL::BN, a.T - t0);
+  B.cols = a.d;
+  B.bytes = clamp_bytes((a.T - t0) * a.d * ESZ);
+
+  // Per-lane state for its NI token columns: running max and sum over the
+  // vocab rows this lane holds, and the target (row index) of each column.
+  float m_run[TL::NI], s_run[TL::NI];
+  int tgt[TL::NI];
+#pragma unroll
+  for (int j = 0; j < TL::NI; ++j) {
+    m_run[j] = kNegInf;
+    s_run[j] = 0.f;
+    const int64_t t = t0 + TL::col_of(wn, j);
+    tgt[j] = t < a.T ? target_code(a.y, t, a.ignore_index, a.V) : -1;
+  }
+
+  TL tile;
+  for (int vt = vt_begin; vt < vt_end; ++vt) {
+    const int64_t v0 = (int64_t)vt * TL::BM;
+    Operand A;
+    A.base = reinterpret_cast<const char*>(a.W) + v0 * a.d * ESZ;
+    A.ld_bytes = (uint32_t)(a.d * ESZ);
+    A.rows = (int)min<int64_t>(TL::BM, a.V - v0);
+    A.cols = a.d;
+    A.bytes = clamp_bytes((a.V - v0) * a.d * ESZ);
+
+    tile.zero();
+    tile.mainloop(A, B, a.d, lds);
+
+    // rows past V (last tile only) do not take part; `lim` is the number of
+    // valid rows counted from this lane's first row
+    if (v0 + TL::BM > a.V) {
+      const int lim = a.V - (int)v0 - wm * TL::WTM - 4 * (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (i * 32 + 8 * (r >> 2) + (r & 3) >= lim)
+#pragma unroll
+            for (int j = 0; j < TL::NI; ++j) tile.acc[i][j][r] = kNegInf;
+    }
+
+    const int wrow0 = (int)v0 + wm * TL::WTM;  // first vocab id of this wave's rows
+#pragma unroll
+    for (int j = 0; j < TL::NI; ++j) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, tile.acc[i][j][r]);
+      const float m_new = fmaxf(m_run[j], mx);
+      if (m_new != kNegInf) {
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sum += fast_exp2((tile.acc[i][j][r] - m_new) * kLog2e);
+        s_run[j] = s_run[j] * fast_exp2((m_run[j] - m_new) * kLog2e) + sum;
+        m_run[j] = m_new;
+      }
+      // target logit, taken from the fp32 accumulator (rare: one tile per token)
+      const int rt = tgt[j] - wrow0 - 4 * (lane >> 5);
+      if (tgt[j] >= wrow0 && tgt[j] < wrow0 + TL::WTM) {
+        float zt = 0.f;
+        bool hit = false;
+#pragma unroll
+        for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (rt == i * 32 + 8 * (r >> 2) + (r & 3)) {
+              zt = tile.acc[i][j][r];
+              hit = true;
+            }
+        if (hit) a.zt[t0 + TL::col_of(wn, j)] = zt;
+      }
+    }
+  }
+
+  // ---- merge the two half-waves (same columns, interleaved rows)
+#pragma unroll
+  for (int j = 0; j < TL::NI; ++j) {
+    const float mo = __shfl_xor(m_run[j], 32);
+    const float so = __shfl_xor(s_run[j], 32);
+    const float mn = fmaxf(m_run[j], mo);
+    if (mn != kNegInf) {
+      s_run[j] = s_run[j] * fast_exp2((m_run[j] - mn) * kLog2e) + so * fast_exp2((mo - mn) * kLog2e);
+      m_run[j] = mn;
+    }
+  }
+  // ---- merge the waves stacked along M through LDS, in ascending wm order
+  float* red = reinterpret_cast<float*>(lds);  // [WM][BN][2]
+  if (lane < 32) {
+#pragma unroll
+    for (int j = 0; j < TL::NI; ++j) {
+      const int c = TL::col_of(wn, j);
+      red[(wm * TL::BN + c) * 2 + 0] = m_run[j];
+      red[(wm * TL::BN + c) * 2 + 1] = s_run[j];
+    }
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < TL::BN; c += TL::NT) {
+    const int64_t t = t0 + c;
+    if (t >= a.T) continue;
+    float M = kNegInf, S = 0.f;
+    for (int w = 0; w < TL::WM; ++w) {
+      const float mw = red[(w * TL::BN + c) * 2 + 0];
+      const float sw = red[(w * TL::BN + c) * 2 + 1];
+      const float mn = fmaxf(M, mw);
+      if (mn != kNegInf) {
+        S = S * fast_exp2((M - mn) * kLog2e) + sw * fast_exp2((mw - mn) * kLog2e);
+        M = mn;
+      }
+    }
+    a.part[((int64_t)split * a.T + t) * 2 + 0] = M;
+    a.part[((int64_t)split * a.T + t) * 2 + 1] = S;
+  }
+}
+
+// ============================================================== forward merge
+__global__ void __launch_bounds__(256) fwd_merge_kernel(MergeArgs a) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= a.T) return;
+  float M = kNegInf, S = 0.f;
+  for (int s = 0; s < a.splits; ++s) {
+    const float ms = a.part[((int64_t)s * a.T + t) * 2 + 0];
+    const float ss = a.part[((int64_t)s * a.T + t) * 2 + 1];
+    const float mn = fmaxf(M, ms);
+    if (mn != kNegInf) {
+      S = S * expf(M - mn) + ss * expf(ms - mn);
+      M = mn;
+    }
+  }
+  const float lse = M + logf(S);
+  a.lse[t] = lse;
+  const int code = target_code(a.y, t, a.ignore_index, a.V);
+  float loss;
+  if (code == -1) loss = 0.f;
+  else if (code == -2) loss = __builtin_nanf("");
+  else loss = lse - a.zt[t];
+  a.loss[t] = loss;
+}
+
+// Fixed-order reduction: thread i sums loss[i], loss[i + 1024], ... in double,
+// then a tree over the 1024 threads.  One workgroup; deterministic.
+__global__ void __launch_bounds__(1024) loss_sum_kernel(const float* loss, int64_t T, float scale,
+                                                        float* out) {
+  __shared__ double buf[1024];
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < T; i += 1024) s += (double)loss[i];
+  buf[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) buf[threadIdx.x] += buf[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = (float)(buf[0] * (double)scale);
+}
+
+// ================================================================ backward dZ
+template <typename E>
+__device__ __forceinline__ void store4(E* p, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4<__bf16>(__bf16* p, float a, float b, float c, float d) {
+  bf16x4_t v = {(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
+  *reinterpret_cast<bf16x4_t*>(p) = v;
+}
+template <>
+__device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<f32x4_t*>(p) = f32x4_t{a, b, c, d};
+}
+
+// One 256 x 256 (vocab x token) tile of the block/slab: recompute logits,
+// form dZ, write it token-major: dz[t_local * ldz + v_local].  Vocab rows past
+// V inside the slab's last tile are written as zeros so the contractions can
+// read whole 16-byte chunks.
+template <typename E>
+__global__ void __launch_bounds__(LogitCfg<E>::T::NT, 1) bwd_dz_kernel(DzArgs a) {
+  using TL = typename LogitCfg<E>::T;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  constexpr int ESZ = TL::ESZ;
+  int tm, tn;
+  if (!xcd_tile(blockIdx.x, a.n_vtiles, a.n_ttiles, 4, tm, tn)) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave / TL::WN, wn = wave % TL::WN;
+  const int64_t v0 = a.v_begin + (int64_t)tm * TL::BM;  // global vocab id of tile row 0
+  const int64_t tl0 = (int64_t)tn * TL::BN;             // token within the block
+  const int64_t t0 = a.t_begin + tl0;                   // global token
+
+  Operand A, B;
+  A.base = reinterpret_cast<const char*>(a.W) + v0 * a.d * ESZ;
+  A.ld_bytes = (uint32_t)(a.d * ESZ);
+  A.rows = (int)max<int64_t>(0, min<int64_t>(TL::BM, a.V - v0));
+  A.cols = a.d;
+  A.bytes = clamp_bytes((a.V - v0) * a.d * ESZ);
+  B.base = reinterpret_cast<const char*>(a.H) + t0 * a.d * ESZ;
+  B.ld_bytes = (uint32_t)(a.d * ESZ);
+  B.rows = (int)min<int64_t>(TL::BN, a.t_count - tl0);
+  B.cols = a.d;
+  B.bytes = clamp_bytes((a.T - t0) * a.d * ESZ);
+
+  TL tile;
+  tile.zero();
+  if (A.rows > 0) tile.mainloop(A, B, a.d, lds);
+
+  const float g = a.grad_scale;
+  E* dz = reinterpret_cast<E*>(a.dz);
+#pragma unroll
+  for (int j = 0; j < TL::NI; ++j) {
+    const int c = TL::col_of(wn, j);
+    const int64_t tl = tl0 + c;
+    if (tl >= a.t_count) continue;
+    const int64_t t = a.t_begin + tl;
+    const int code = target_code(a.y, t, a.ignore_index, a.V);
+    const float lse = a.lse[t];
+    const float scale = code == -1 ? 0.f : (code == -2 ? __builtin_nanf("") : g);
+    const int rt = code - (int)v0;  // target row within the workgroup tile
+#pragma unroll
+    for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        float o[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = rq * 4 + u;
+          const int row = TL::row_of(wm, i, r);
+          float p = fast_exp2((tile.acc[i][j][r] - lse) * kLog2e);
+          float val = scale * p;
+          if (row == rt) val -= scale;
+          if (v0 + row >= a.V) val = 0.f;
+          o[u] = val;
+        }
+        const int row0 = TL::row_of(wm, i, rq * 4);
+        const int64_t vl = v0 - a.v_begin + row0;  // vocab within the slab
+        if (vl < a.ldz_cols)
+          store4<E>(dz + tl * a.ldz + vl, o[0], o[1], o[2], o[3]);
+      }
+  }
+  (void)lane;
+}
+
+// ================================================================ backward dH
+// dH[block] (+)= dZ[block, slab] * W[slab].  M = tokens, N = hidden, K = slab.
+// mode: 0 = first slab of several (write fp32 acc), 1 = middle (acc += ),
+// 2 = last of several (acc + partial -> dH in E), 3 = only slab (-> dH in E).
+template <typename E>
+__global__ void __launch_bounds__(DhCfg<E>::T::NT, 1) bwd_dh_kernel(DhArgs a) {
+  using TL = typename DhCfg<E>::T;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  constexpr int ESZ = TL::ESZ;
+  int tm, tn;
+  if (!xcd_tile(blockIdx.x, a.n_mtiles, a.n_ntiles, 4, tm, tn)) return;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / TL::WN, wn = wave % TL::WN;
+  const int64_t tl0 = (int64_t)tm * TL::BM;  // token within block
+  const int64_t n0 = (int64_t)tn * TL::BN;   // hidden index
+
+  Operand A, B;
+  A.base = reinterpret_cast<const char*>(a.dz) + tl0 * a.ldz * ESZ;
+  A.ld_bytes = (uint32_t)(a.ldz * ESZ);
+  A.rows = (int)min<int64_t>(TL::BM, a.t_count - tl0);
+  A.cols = a.k_count;
+  A.bytes = clamp_bytes((a.t_count - tl0) * a.ldz * ESZ);
+  B.base = reinterpret_cast<const char*>(a.W) + (a.v_begin * a.d + n0) * ESZ;
+  B.ld_bytes = (uint32_t)(a.d * ESZ);
+  B.rows = a.k_count;
+  B.cols = (int)min<int64_t>(TL::BN, a.d - n0);
+  B.bytes = clamp_bytes(((int64_t)(a.V - a.v_begin) * a.d - n0) * ESZ);
+
+  TL tile;
+  tile.zero();
+  tile.mainloop(A, B, a.k_count, lds);
+
+#pragma unroll
+  for (int j = 0; j < TL::NI; ++j) {
+    const int64_t n = n0 + TL::col_of(wn, j);
+    if (n >= a.d) continue;
+#pragma unroll
+    for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t tl = tl0 + TL::row_of(wm, i, r);
+        if (tl >= a.t_count) continue;
+        float v = tile.acc[i][j][r];
+        float* accp = a.dh_acc + tl * a.d + n;
+        if (a.mode == 1 || a.mode == 2) v += *accp;
+        if (a.mode == 0 || a.mode == 1) {
+          *accp = v;
+        } else {
+          E* out = reinterpret_cast<E*>(a.dH) + (a.t_begin + tl) * a.d + n;
+          *out = (E)v;
+        }
+      }
+  }
+}
+
+// ================================================================ backward dW
+// dW[slab] (+)= dZ[block, slab]^T * H[block].  M = slab vocab, N = hidden,
+// K = block tokens.  accumulate: 0 = overwrite, 1 = add to dW.
+template <typename E>
+__global__ void __launch_bounds__(DwCfg<E>::T::NT, 1) bwd_dw_kernel(DwArgs a) {
+  using TL = typename DwCfg<E>::T;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  constexpr int ESZ = TL::ESZ;
+  int tm, tn;
+  if (!xcd_tile(blockIdx.x, a.n_mtiles, a.n_ntiles, 4, tm, tn)) return;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / TL::WN, wn = wave % TL::WN;
+  const int64_t vl0 = (int64_t)tm * TL::BM;  // vocab within slab
+  const int64_t n0 = (int64_t)tn * TL::BN;
+
+  Operand A, B;
+  A.base = reinterpret_cast<const char*>(a.dz) + vl0 * ESZ;
+  A.ld_bytes = (uint32_t)(a.ldz * ESZ);
+  A.rows = a.t_count;
+  A.cols = (int)min<int64_t>(TL::BM, a.ldz - vl0);
+  A.bytes = clamp_bytes((int64_t)a.t_count * a.ldz * ESZ - vl0 * ESZ);
+  B.base = reinterpret_cast<const char*>(a.H) + (a.t_begin * a.d + n0) * ESZ;
+  B.ld_bytes = (uint32_t)(a.d * ESZ);
+  B.rows = a.t_count;
+  B.cols = (int)min<int64_t>(TL::BN, a.d - n0);
+  B.bytes = clamp_bytes(((a.T - a.t_begin) * a.d - n0) * ESZ);
+
+  TL tile;
+  tile.zero();
+  tile.mainloop(A, B, a.t_count, lds);
+
+#pragma unroll
+  for (int j = 0; j < TL::NI; ++j) {
+    const int64_t n = n0 + TL::col_of(wn, j);
+    if (n >= a.d) continue;
+#pragma unroll
+    for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t vl = vl0 + TL::row_of(wm, i, r);
+        if (vl >= a.v_count) continue;
+        float* p = a.dW + (a.v_begin + vl) * a.d + n;
+        float v = tile.acc[i][j][r];
+        if (a.accumulate) v += *p;
+        *p = v;
+      }
+  }
+}
+
+__global__ void __launch_bounds__(256) fill_zero_kernel(float* p, int64_t n) {
+  const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  const int64_t stride = (int64_t)gridDim.x * 256 * 4;
+  for (int64_t i = i0; i < n; i += stride) {
+    if (i + 4 <= n) {
+      *reinterpret_cast<f32x4_t*>(p + i) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    } else {
+      for (int64_t k = i; k < n; ++k) p[k] = 0.f;
+    }
+  }
+}
+
+// ================================================================== launchers
+template <typename K, typename Args>
+static hipError_t launch(K kernel, int grid, int threads, int lds, hipStream_t s, const Args& args) {
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), lds, s, args);
+  return hipGetLastError();
+}
+
+template <typename K>
+static hipError_t set_lds(K kernel, int bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+hipError_t launch_fwd_sweep(const FwdArgs& a, bool bf16, int grid, hipStream_t s) {
+  if (bf16) {
+    using TL = LogitCfg<__bf16>::T;
+    hipError_t e = set_lds(fwd_sweep_kernel<__bf16>, TL::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    return launch(fwd_sweep_kernel<__bf16>, grid, TL::NT, TL::LDS_BYTES, s, a);
+  }
+  using TL = LogitCfg<float>::T;
+  hipError_t e = set_lds(fwd_sweep_kernel<float>, TL::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  return launch(fwd_sweep_kernel<float>, grid, TL::NT, TL::LDS_BYTES, s, a);
+}
+
+hipError_t launch_fwd_merge(const MergeArgs& a, hipStream_t s) {
+  return launch(fwd_merge_kernel, (int)((a.T + 255) / 256), 256, 0, s, a);
+}
+
+hipError_t launch_loss_sum(const float* loss, int64_t T, float scale, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(loss_sum_kernel, dim3(1), dim3(1024), 0, s, loss, T, scale, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dz(const DzArgs& a, bool bf16, hipStream_t s) {
+  const int grid = xcd_grid(a.n_vtiles, a.n_ttiles);
+  if (bf16) {
+    using TL = LogitCfg<__bf16>::T;
+    hipError_t e = set_lds(bwd_dz_kernel<__bf16>, TL::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    return launch(bwd_dz_kernel<__bf16>, grid, TL::NT, TL::LDS_BYTES, s, a);
+  }
+  using TL = LogitCfg<float>::T;
+  hipError_t e = set_lds(bwd_dz_kernel<float>, TL::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  return launch(bwd_dz_kernel<float>, grid, TL::NT, TL::LDS_BYTES, s, a);
+}
+
+hipError_t launch_bwd_dh(const DhArgs& a, bool bf16, hipStream_t s) {
+  const int grid = xcd_grid(a.n_mtiles, a.n_ntiles);
+  if (bf16) {
+    using TL = DhCfg<__bf16>::T;
+    hipError_t e = set_lds(bwd_dh_kernel<__bf16>, TL::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    return launch(bwd_dh_kernel<__bf16>, grid, TL::NT, TL::LDS_BYTES, s, a);
+  }
+  using TL = DhCfg<float>::T;
+  hipError_t e = set_lds(bwd_dh_kernel<float>, TL::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  return launch(bwd_dh_kernel<float>, grid, TL::NT, TL::LDS_BYTES, s, a);
+}
+
+hipError_t launch_bwd_dw(const DwArgs& a, bool bf16, hipStream_t s) {
+  const int grid = xcd_grid(a.n_mtiles, a.n_ntiles);
+  if (bf16) {
+    using TL = DwCfg<__bf16>::T;
+    hipError_t e = set_lds(bwd_dw_kernel<__bf16>, TL::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    return launch(bwd_dw_kernel<__bf16>, grid, TL::NT, TL::LDS_BYTES, s, a);
+  }
+  using TL = DwCfg<float>::T;
+  hipError_t e = set_lds(bwd_dw_kernel<float>, TL::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  return launch(bwd_dw_kernel<float>, grid, TL::NT, TL::LDS_BYTES, s, a);
+}
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n / 4 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+TileInfo tile_info(bool bf16) {
+  TileInfo t;
+  if (bf16) {
+    t.logit_bm = LogitCfg<__bf16>::T::BM;
+    t.logit_bn = LogitCfg<__bf16>::T::BN;
+    t.dh_bm = DhCfg<__bf16>::T::BM;
+    t.dh_bn = DhCfg<__bf16>::T::BN;
+    t.dw_bm = DwCfg<__bf16>::T::BM;
+    t.dw_bn = DwCfg<__bf16>::T::BN;
+  } else {
+    t.logit_bm = LogitCfg<float>::T::BM;
+    t.logit_bn = LogitCfg<float>::T::BN;
+    t.dh_bm = DhCfg<float>::T::BM;
+    t.dh_bn = DhCfg<float>::T::BN;
+    t.dw_bm = DwCfg<float>::T::BM;
+    t.dw_bn = DwCfg<float>::T::BN;
+  }
+  return t;
+}
+
+}  // namespace flce

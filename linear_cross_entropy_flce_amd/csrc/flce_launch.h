@@ -1,0 +1,95 @@
+// flce_launch.h -- internal interface between the host sequencing (flce_api.cpp)
+// and the kernels (flce_kernels.hip).  Not part of the public C-ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flce {
+
+struct FwdArgs {
+  const void* H;
+  const void* W;
+  const int64_t* y;
+  int64_t ignore_index;
+  int64_t T;
+  int d, V;
+  int n_ttiles, n_vtiles;
+  int splits, tps, grp;
+  float* part;  // [splits][T][2] running (max, sum)
+  float* zt;    // [T] target logits
+};
+
+struct MergeArgs {
+  const float* part;
+  const float* zt;
+  const int64_t* y;
+  int64_t ignore_index;
+  int64_t T;
+  int V, splits;
+  float* loss;
+  float* lse;
+};
+
+struct DzArgs {
+  const void* H;
+  const void* W;
+  const int64_t* y;
+  const float* lse;
+  int64_t ignore_index;
+  int64_t T;
+  int d, V;
+  int64_t t_begin;  // first token of the block
+  int t_count;      // tokens in the block
+  int64_t v_begin;  // first vocab id of the slab
+  int n_vtiles, n_ttiles;
+  int64_t ldz;       // dZ row pitch (elements)
+  int64_t ldz_cols;  // columns of each dZ row that this call writes
+  float grad_scale;
+  void* dz;
+};
+
+struct DhArgs {
+  const void* dz;
+  const void* W;
+  int64_t ldz;
+  int d, V;
+  int64_t t_begin;
+  int t_count;
+  int64_t v_begin;
+  int k_count;  // vocab rows in the slab (K)
+  int n_mtiles, n_ntiles;
+  int mode;     // 0 first of several, 1 middle, 2 last of several, 3 only
+  float* dh_acc;
+  void* dH;
+};
+
+struct DwArgs {
+  const void* dz;
+  const void* H;
+  int64_t ldz;
+  int64_t T;
+  int d;
+  int64_t t_begin;
+  int t_count;   // K
+  int64_t v_begin;
+  int v_count;   // M
+  int n_mtiles, n_ntiles;
+  int accumulate;
+  float* dW;
+};
+
+struct TileInfo {
+  int logit_bm, logit_bn, dh_bm, dh_bn, dw_bm, dw_bn;
+};
+
+TileInfo tile_info(bool bf16);
+hipError_t launch_fwd_sweep(const FwdArgs& a, bool bf16, int grid, hipStream_t s);
+hipError_t launch_fwd_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_loss_sum(const float* loss, int64_t T, float scale, float* out, hipStream_t s);
+hipError_t launch_bwd_dz(const DzArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_bwd_dh(const DhArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_bwd_dw(const DwArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+
+}  // namespace flce

@@ -1,0 +1,97 @@
+"""Helpers shared by the GPU tests: upload seeded inputs, run the library
+through its C-ABI binding, compare with the oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import linear_cross_entropy_flce_amd as flce
+import workloads as wl
+
+# Tolerances fixed for this operation: per-token loss and lse absolute error,
+# and relative Frobenius error of dH and dW, by input precision.
+TOL = {
+    wl.DTYPE_BF16: dict(loss=2e-3, grad=1e-2),
+    wl.DTYPE_F32: dict(loss=1e-5, grad=1e-5),
+}
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def device_inputs(inp: wl.Inputs):
+    if inp.dtype == wl.DTYPE_BF16:
+        H = torch.from_numpy(inp.H.view(np.int16)).cuda().view(torch.bfloat16)
+        W = torch.from_numpy(inp.W.view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        H = torch.from_numpy(inp.H).cuda()
+        W = torch.from_numpy(inp.W).cuda()
+    y = torch.from_numpy(inp.y).cuda()
+    return H, W, y
+
+
+def run_gpu(inp: wl.Inputs, loss_scale=1.0, grad_scale=1.0, cap=0, backward=True, dev=None,
+            accumulate_dW=False, dW_init=None):
+    """One forward (+ backward) through the C-ABI.  Returns numpy results."""
+    H, W, y = dev if dev is not None else device_inputs(inp)
+    plan = flce.flce_plan(inp.T, inp.d, inp.V, inp.dtype, cap)
+    ws = flce.workspace(plan, W.device)
+    red = torch.empty(1, dtype=torch.float32, device=W.device)
+    loss, lse, _ = flce.flce_forward(plan, H, W, y, inp.ignore_index, loss_scale,
+                                     loss_reduced=red, ws=ws)
+    out = dict(plan=plan, loss=loss, lse=lse, red=red)
+    if backward:
+        dW = None
+        if dW_init is not None:
+            dW = torch.from_numpy(dW_init).cuda()
+        dH, dW = flce.flce_backward(plan, H, W, y, lse, inp.ignore_index, grad_scale, dW=dW,
+                                    accumulate_dW=accumulate_dW, ws=ws)
+        out.update(dH=dH, dW=dW)
+    torch.cuda.synchronize()
+    return {k: (v.float().cpu().numpy() if isinstance(v, torch.Tensor) else v)
+            for k, v in out.items()}
+
+
+def max_abs(a, b, mask=None):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    if mask is not None:
+        a, b = a[mask], b[mask]
+    return float(np.max(np.abs(a - b))) if a.size else 0.0
+
+
+def rel_fro(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    nb = np.linalg.norm(b)
+    d = np.linalg.norm(a - b)
+    if nb == 0.0:
+        return d
+    return float(d / nb)
+
+
+def compare(got, ref, dtype, what=("loss", "lse", "dH", "dW"), rows=None):
+    """Asserts the tolerances; returns the error figures."""
+    tol = TOL[dtype]
+    errs = {}
+    loss_ref, lse_ref = ref["loss"], ref["lse"]
+    if "loss" in what:
+        g = got["loss"] if rows is None else got["loss"][rows]
+        errs["loss"] = max_abs(g, loss_ref)
+        assert errs["loss"] <= tol["loss"], errs
+    if "lse" in what:
+        g = got["lse"] if rows is None else got["lse"][rows]
+        errs["lse"] = max_abs(g, lse_ref)
+        assert errs["lse"] <= tol["loss"], errs
+    if "dH" in what:
+        g = got["dH"] if rows is None else got["dH"][rows]
+        errs["dH"] = rel_fro(g, ref["dH"])
+        assert errs["dH"] <= tol["grad"], errs
+    if "dW" in what:
+        errs["dW"] = rel_fro(got["dW"], ref["dW"])
+        assert errs["dW"] <= tol["grad"], errs
+    return errs

@@ -1,0 +1,159 @@
+"""Host-side tests of the C-ABI library: symbols, planner, validation.
+
+None of these launches a kernel: every call either plans (host-only integer
+arithmetic) or fails validation before anything reaches the GPU.
+"""
+import ctypes
+import json
+import os
+import re
+import subprocess
+
+import pytest
+
+import linear_cross_entropy_flce_amd as flce
+import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flce.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "pages_memory_figures.json")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(flce._lib.LIB_PATH):
+        from linear_cross_entropy_flce_amd import build
+        build.build()
+    return flce.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S.*?\b(flce_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(flce.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", flce._lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for name in declared_functions():
+        assert name in syms, name
+        assert getattr(lib, name) is not None
+
+
+def test_plan_struct_size_matches_header(lib):
+    # 3 int64 + 6 int32 + 4 int64 + 7 uint64 + 2 uint32
+    assert ctypes.sizeof(flce.Plan) == 3 * 8 + 6 * 4 + 4 * 8 + 7 * 8 + 2 * 4
+
+
+def test_version_and_status_strings(lib):
+    assert flce.version() == "0.1.0"
+    for st in (0, -1, -2, -3, -4):
+        assert lib.flce_status_string(st)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((-1, 128, 1000, 1), flce.FLCE_ERR_INVALID_ARG),
+    ((10, 0, 1000, 1), flce.FLCE_ERR_INVALID_ARG),
+    ((10, 128, 0, 1), flce.FLCE_ERR_INVALID_ARG),
+    ((10, 128, 1000, 7), flce.FLCE_ERR_INVALID_ARG),
+    ((10, 12, 1000, 1), flce.FLCE_ERR_UNSUPPORTED),
+    ((10, 65544, 1000, 1), flce.FLCE_ERR_UNSUPPORTED),
+    ((1 << 31, 128, 1000, 1), flce.FLCE_ERR_UNSUPPORTED),
+])
+def test_plan_rejects(lib, args, status):
+    st, _ = flce.flce_plan_status(*args)
+    assert st == status
+    assert flce.last_error()
+
+
+def test_plan_null_out(lib):
+    assert lib.flce_plan(10, 128, 1000, 1, 0, None) == flce.FLCE_ERR_INVALID_ARG
+
+
+def test_plan_cap_too_small(lib):
+    st, _ = flce.flce_plan_status(65536, 2048, 124160, flce.FLCE_BF16, cap=1000)
+    assert st == flce.FLCE_ERR_WORKSPACE
+    assert "cap" in flce.last_error()
+
+
+@pytest.mark.parametrize("cfg", wl.CONFIGS, ids=lambda c: c.name)
+def test_plan_invariants_on_configs(lib, cfg):
+    p = flce.flce_plan(cfg.T, cfg.d, cfg.V, cfg.dtype)
+    esz = 2 if cfg.dtype == wl.DTYPE_BF16 else 4
+    # vocab-axis workspace below 1 GB, and exactly [block x slab]
+    assert p.bwd_ws_bytes < 10 ** 9
+    assert p.dz_ws_bytes == p.bwd_block * p.bwd_slab * esz
+    assert p.dh_acc_bytes == (p.bwd_block * cfg.d * 4 if p.n_slabs > 1 else 0)
+    # blocks and slabs are tile multiples and cover T and V
+    assert p.bwd_block % p.tile_t == 0 and p.bwd_slab % p.tile_v == 0
+    assert p.n_blocks * p.bwd_block >= cfg.T > (p.n_blocks - 1) * p.bwd_block
+    assert p.n_slabs * p.bwd_slab >= cfg.V > (p.n_slabs - 1) * p.bwd_slab
+    # forward splits cover the vocab tiles, none empty
+    n_vt = -(-cfg.V // p.tile_v)
+    assert p.fwd_splits * p.fwd_tiles_per_split >= n_vt
+    assert (p.fwd_splits - 1) * p.fwd_tiles_per_split < n_vt
+    assert p.ws_bytes == max(p.fwd_ws_bytes, p.bwd_ws_bytes)
+
+
+def test_plan_blocks_of_the_pages_shape(lib):
+    """65,536 tokens x 124,160 vocab: 8 blocks of 8,192 tokens x 3 slabs."""
+    p = flce.flce_plan(65536, 2048, 124160, "bf16")
+    assert (p.bwd_block, p.n_blocks, p.n_slabs, p.bwd_slab) == (8192, 8, 3, 41472)
+    assert p.dz_ws_bytes == 8192 * 41472 * 2
+
+
+def test_naive_footprint_matches_pages(lib):
+    """The pages' printed figures for the materialised logits."""
+    g = json.load(open(GOLDEN))
+    for it in g["items"]:
+        dt = "bf16" if it["bytes_per_elem"] == 2 else "f32"
+        p = flce.flce_plan(it["T"], 128, it["V"], dt)
+        total = p.naive_logits_bytes * it["copies"]
+        assert round(total / 1e9, 2) == it["GB_decimal"], it
+        if "GiB" in it:
+            # the page's GiB figure is within 0.01 of the exact 30.3125
+            assert abs(total / 2 ** 30 - it["GiB"]) < 0.01
+    va = g["vocab_alignment"]
+    assert va["V"] == va["factor"] * va["quotient"]
+
+
+def test_cap_is_honoured(lib):
+    for cap in (50_000_000, 200_000_000, 950_000_000):
+        p = flce.flce_plan(65536, 2048, 124160, "bf16", cap)
+        assert p.bwd_ws_bytes <= cap
+
+
+def _fwd(lib, plan, H=16, W=16, y=16, loss=16, lse=16, ws=16, ws_bytes=1 << 40):
+    return lib.flce_forward(ctypes.byref(plan) if plan is not None else None, H, W, y, -100, 1.0,
+                            loss, lse, None, ws, ws_bytes, None)
+
+
+def test_forward_validation(lib):
+    p = flce.flce_plan(100, 64, 1000, "bf16")
+    assert _fwd(lib, None) == flce.FLCE_ERR_INVALID_ARG
+    bad = flce.Plan()
+    assert _fwd(lib, bad) == flce.FLCE_ERR_INVALID_ARG
+    assert _fwd(lib, p, W=None) == flce.FLCE_ERR_INVALID_ARG
+    assert _fwd(lib, p, H=None) == flce.FLCE_ERR_INVALID_ARG
+    assert _fwd(lib, p, loss=None) == flce.FLCE_ERR_INVALID_ARG
+    assert _fwd(lib, p, H=24) == flce.FLCE_ERR_UNSUPPORTED
+    assert _fwd(lib, p, ws_bytes=p.fwd_ws_bytes - 1) == flce.FLCE_ERR_WORKSPACE
+
+
+def _bwd(lib, plan, H=16, W=16, y=16, lse=16, dH=16, dW=16, ws=16, ws_bytes=1 << 40):
+    return lib.flce_backward(ctypes.byref(plan), H, W, y, lse, -100, 1.0, dH, dW, 0, ws, ws_bytes,
+                             None)
+
+
+def test_backward_validation(lib):
+    p = flce.flce_plan(100, 64, 1000, "bf16")
+    assert _bwd(lib, flce.Plan()) == flce.FLCE_ERR_INVALID_ARG
+    assert _bwd(lib, p, dW=None) == flce.FLCE_ERR_INVALID_ARG
+    assert _bwd(lib, p, lse=None) == flce.FLCE_ERR_INVALID_ARG
+    assert _bwd(lib, p, dW=20) == flce.FLCE_ERR_UNSUPPORTED
+    assert _bwd(lib, p, ws_bytes=p.bwd_ws_bytes - 1) == flce.FLCE_ERR_WORKSPACE

@@ -1,0 +1,231 @@
+"""GPU parity: the HIP library (through its C-ABI) against the CPU oracle.
+
+Element-by-element on shapes that span several tiles and ragged tails, the
+edge cases of the method, and the five workload configurations (in full for
+the three smaller ones, on seeded row samples at full size for the two
+largest).  Tolerances: loss/lse absolute 2e-3 (bf16) / 1e-5 (fp32); dH, dW
+relative Frobenius 1e-2 (bf16) / 1e-5 (fp32).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from gpu_helpers import TOL, compare, device_inputs, log, max_abs, rel_fro, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+IGN = wl.IGNORE_INDEX
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_cross_entropy_flce_amd as flce
+    flce.load()
+    yield
+    torch.cuda.empty_cache()
+
+
+def _ref(inp, g):
+    loss, lse, dH, dW = oracle.forward_backward(inp.H_f32(), inp.W_f32(), inp.y, IGN, g)
+    return dict(loss=loss, lse=lse, dH=dH, dW=dW)
+
+
+UNIT = [
+    # T, d, V, ignore fraction
+    (1, 8, 1, 0.0),
+    (1, 8, 2, 0.0),
+    (5, 16, 7, 0.0),
+    (63, 72, 1000, 0.2),
+    (257, 128, 1000, 0.0),
+    (300, 136, 515, 0.3),
+    (257, 72, 32007, 0.1),
+    (520, 64, 2049, 0.0),
+]
+
+
+@pytest.mark.parametrize("dtype", [wl.DTYPE_F32, wl.DTYPE_BF16])
+@pytest.mark.parametrize("T,d,V,ign", UNIT, ids=lambda v: str(v))
+def test_unit_shapes(T, d, V, ign, dtype):
+    log(f"unit T={T} d={d} V={V} ign={ign} {dtype}")
+    inp = wl.make_inputs(T, d, V, dtype, seed=100 + T + d + V, sigma_w=0.5, ignore_frac=ign)
+    g = 1.0 / max(1, T)
+    got = run_gpu(inp, loss_scale=g, grad_scale=g)
+    ref = _ref(inp, g)
+    errs = compare(got, ref, dtype)
+    red = oracle.reduced_loss(ref["loss"], g)
+    assert abs(got["red"][0] - red) <= TOL[dtype]["loss"] * max(1.0, abs(red))
+    log("  errors", errs)
+
+
+@pytest.mark.parametrize("dtype", [wl.DTYPE_F32, wl.DTYPE_BF16])
+def test_targets_at_tile_edges(dtype):
+    T, d, V = 64, 32, 1030
+    inp = wl.make_inputs(T, d, V, dtype, seed=7, sigma_w=0.5)
+    edges = [0, 1, 31, 32, 63, 64, 127, 128, 255, 256, 257, 511, 512, 767, 768, 1023, 1024, V - 1]
+    inp.y[:] = np.array([edges[i % len(edges)] for i in range(T)])
+    got = run_gpu(inp, grad_scale=0.5)
+    compare(got, _ref(inp, 0.5), dtype)
+
+
+@pytest.mark.parametrize("dtype", [wl.DTYPE_F32, wl.DTYPE_BF16])
+def test_all_ignored_and_none_ignored(dtype):
+    inp = wl.make_inputs(130, 40, 600, dtype, seed=11, sigma_w=0.3)
+    inp.y[:] = IGN
+    got = run_gpu(inp)
+    assert np.all(got["loss"] == 0.0)
+    assert np.all(got["dH"] == 0.0) and np.all(got["dW"] == 0.0)
+    ref = _ref(inp, 1.0)
+    assert max_abs(got["lse"], ref["lse"]) <= TOL[dtype]["loss"]
+    inp2 = wl.make_inputs(130, 40, 600, dtype, seed=12, sigma_w=0.3)
+    compare(run_gpu(inp2), _ref(inp2, 1.0), dtype)
+
+
+def test_large_logits_running_max():
+    """Shift every row of W by c with h . c near 100 (fp32) or 400 (bf16):
+    logits far beyond exp()'s float range; lse shifts by h . c, loss and
+    gradients do not change.  A kernel without the running max overflows."""
+    for dtype, target in ((wl.DTYPE_F32, 100.0), (wl.DTYPE_BF16, 400.0)):
+        inp = wl.make_inputs(200, 64, 900, dtype, seed=13, sigma_w=0.2)
+        H = inp.H_f32().astype(np.float64)
+        c = np.zeros(64)
+        c[0] = target / np.abs(H[:, 0]).max()
+        W = inp.W_f32().astype(np.float64) + c
+        if dtype == wl.DTYPE_F32:
+            inp.W = W.astype(np.float32)
+        else:
+            inp.W = wl.f32_to_bf16_bits(W.astype(np.float32))
+        got = run_gpu(inp)
+        ref = _ref(inp, 1.0)
+        assert np.all(np.isfinite(got["loss"])) and np.all(np.isfinite(got["lse"]))
+        # loss tolerance scales with the ulp of |lse| (float32 arithmetic)
+        tl = TOL[dtype]["loss"] + 4 * np.abs(ref["lse"]).max() * 2.0 ** -23
+        assert max_abs(got["loss"], ref["loss"]) <= tl
+        assert max_abs(got["lse"], ref["lse"]) <= tl
+        assert rel_fro(got["dH"], ref["dH"]) <= 2 * TOL[dtype]["grad"]
+        assert rel_fro(got["dW"], ref["dW"]) <= 2 * TOL[dtype]["grad"]
+
+
+@pytest.mark.parametrize("dtype", [wl.DTYPE_F32, wl.DTYPE_BF16])
+def test_several_blocks_and_slabs(dtype):
+    """A small workspace cap forces several token blocks and vocab slabs: the
+    fp32 dH accumulator and the block-ordered dW accumulation are exercised."""
+    T, d, V = 1100, 96, 3000
+    inp = wl.make_inputs(T, d, V, dtype, seed=17, sigma_w=0.4, ignore_frac=0.1)
+    esz = 4 if dtype == wl.DTYPE_F32 else 2
+    cap = 512 * 1024 * esz + 512 * d * 4
+    got = run_gpu(inp, grad_scale=0.25, cap=cap)
+    plan = got["plan"]
+    log("plan", plan.n_blocks, plan.n_slabs, plan.bwd_block, plan.bwd_slab)
+    assert plan.n_blocks >= 2 and plan.n_slabs >= 2
+    compare(got, _ref(inp, 0.25), dtype)
+
+
+@pytest.mark.parametrize("dtype", [wl.DTYPE_F32, wl.DTYPE_BF16])
+def test_accumulate_dW(dtype):
+    inp = wl.make_inputs(300, 48, 700, dtype, seed=19, sigma_w=0.4)
+    base = np.random.default_rng(0).standard_normal((700, 48)).astype(np.float32)
+    got = run_gpu(inp, accumulate_dW=True, dW_init=base)
+    ref = _ref(inp, 1.0)
+    ref["dW"] = ref["dW"] + base
+    compare(got, ref, dtype)
+
+
+def test_deterministic():
+    inp = wl.make_inputs(700, 256, 5000, wl.DTYPE_BF16, seed=23, ignore_frac=0.1)
+    dev = device_inputs(inp)
+    a = run_gpu(inp, grad_scale=0.01, dev=dev)
+    b = run_gpu(inp, grad_scale=0.01, dev=dev)
+    for k in ("loss", "lse", "dH", "dW"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_zero_weights_closed_form():
+    """W = 0 on the GPU: lse = loss = ln V exactly (up to float rounding)."""
+    inp = wl.make_inputs(256, 64, 3000, wl.DTYPE_BF16, seed=29)
+    inp.W[:] = 0
+    got = run_gpu(inp)
+    assert max_abs(got["lse"], math.log(3000)) <= 1e-5
+    assert max_abs(got["loss"], math.log(3000)) <= 1e-5
+    assert np.all(got["dH"] == 0.0)
+
+
+# ------------------------------------------------------------------ configs
+
+@pytest.mark.parametrize("ci", [0, 1])
+def test_config_full(ci):
+    cfg = wl.CONFIGS[ci]
+    log(f"config {ci} {cfg.name}: inputs")
+    inp = wl.config_inputs(cfg)
+    ls, gs = cfg.scales()
+    got = run_gpu(inp, loss_scale=ls, grad_scale=gs)
+    log("  oracle")
+    ref = _ref(inp, gs)
+    errs = compare(got, ref, cfg.dtype)
+    red = oracle.reduced_loss(ref["loss"], ls)
+    assert abs(got["red"][0] - red) <= TOL[cfg.dtype]["loss"] * max(1.0, abs(red))
+    log("  errors", errs)
+
+
+@pytest.mark.timeout(900)
+def test_config2_full():
+    cfg = wl.CONFIGS[2]
+    log(f"config 2 {cfg.name}: inputs")
+    inp = wl.config_inputs(cfg)
+    ls, gs = cfg.scales()
+    got = run_gpu(inp, loss_scale=ls, grad_scale=gs)
+    log("  oracle (full, row chunks)")
+    last = [0]
+
+    def progress(r, T):
+        if r - last[0] >= 2048 or r == T:
+            last[0] = r
+            log(f"  oracle rows {r}/{T}")
+
+    loss, lse, dH, dW = oracle.forward_backward(inp.H_f32(), inp.W_f32(), inp.y, IGN, gs,
+                                                progress=progress)
+    errs = compare(got, dict(loss=loss, lse=lse, dH=dH, dW=dW), cfg.dtype)
+    log("  errors", errs)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("ci", [3, 4])
+def test_config_sampled(ci):
+    """Full-size run; the oracle checks 256 seeded rows (loss, lse, dH) and a
+    seeded 2,048-token sub-batch run through both paths (dW).  At full size
+    the dW rows must sum to zero (each dZ row sums to zero)."""
+    cfg = wl.CONFIGS[ci]
+    log(f"config {ci} {cfg.name}: inputs")
+    inp = wl.config_inputs(cfg)
+    ls, gs = cfg.scales()
+    log("  gpu full size")
+    got = run_gpu(inp, loss_scale=ls, grad_scale=gs)
+    assert np.all(np.isfinite(got["loss"])) and np.all(np.isfinite(got["dW"]))
+    rows = wl.sample_rows(cfg, 256)
+    log("  oracle rows")
+    Hf = inp.H_f32()
+    Wf = inp.W_f32()
+    loss, lse, dH = oracle.rows_forward_dH(Hf, Wf, inp.y, rows, IGN, gs)
+    errs = compare(got, dict(loss=loss, lse=lse, dH=dH), cfg.dtype, what=("loss", "lse", "dH"),
+                   rows=rows)
+    log("  row errors", errs)
+    # sum over the vocab of dW is zero up to fp32/bf16 rounding
+    colsum = got["dW"].astype(np.float64).sum(axis=0)
+    scale = np.abs(got["dW"]).astype(np.float64).sum(axis=0).max()
+    assert np.abs(colsum).max() <= 1e-3 * scale
+    del got
+    torch.cuda.empty_cache()
+    # dW on a 2,048-token sub-batch through both paths
+    sub = np.sort(wl.streams(cfg.seed_base + cfg.index)[4].choice(cfg.T, 2048, replace=False))
+    sinp = inp.rows(sub)
+    log("  gpu sub-batch")
+    sg = run_gpu(sinp, loss_scale=ls, grad_scale=gs)
+    log("  oracle sub-batch")
+    sref = _ref(sinp, gs)
+    errs = compare(sg, sref, cfg.dtype)
+    log("  sub-batch errors", errs)
