@@ -127,6 +127,32 @@ flce_status_t flce_backward(const flce_plan_t* plan, const void* H, const void* 
                             float grad_scale, void* dH, float* dW, int accumulate_dW, void* ws,
                             uint64_t ws_bytes, void* stream);
 
+/* ---- kernel timing (a profiling aid; off by default) --------------------
+ * While enabled, every kernel launch made by flce_forward / flce_backward on
+ * the calling process is bracketed by two hipEvents recorded on the caller's
+ * stream, and tagged with the algorithmic work of that launch.
+ * flce_timing_collect() waits for the recorded events, adds each launch's
+ * elapsed time to its kernel's entry, fills up to `max_entries` entries
+ * (one per kernel name, in a fixed order) and clears the record.  The
+ * registry is process-global and mutex-protected; it is the only shared
+ * state of the library.  Events are created by the library the first time
+ * they are needed and reused; no device memory is allocated. */
+typedef struct flce_kernel_time {
+  char name[24];     /* kernel name, e.g. "fwd_sweep" */
+  int64_t launches;  /* launches recorded since the last collect */
+  double total_ms;   /* summed event-to-event time of those launches */
+  double flops;      /* algorithmic flops of those launches (2*M*N*K each) */
+  double bytes;      /* algorithmic HBM bytes of those launches */
+} flce_kernel_time_t;
+
+/* Turns timing on (nonzero) or off (0).  Returns FLCE_OK. */
+flce_status_t flce_timing_enable(int enable);
+
+/* Collects and clears the record; *n_out receives the number of entries
+ * written.  FLCE_ERR_INVALID_ARG for NULL pointers, FLCE_ERR_HIP when an
+ * event query fails. */
+flce_status_t flce_timing_collect(flce_kernel_time_t* out, int max_entries, int* n_out);
+
 /* Static description of a status code. */
 const char* flce_status_string(flce_status_t status);
 

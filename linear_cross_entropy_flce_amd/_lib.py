@@ -22,8 +22,8 @@ FLCE_ERR_UNSUPPORTED = -2
 FLCE_ERR_WORKSPACE = -3
 FLCE_ERR_HIP = -4
 
-EXPORTED = ["flce_plan", "flce_forward", "flce_backward", "flce_status_string",
-            "flce_last_error", "flce_version"]
+EXPORTED = ["flce_plan", "flce_forward", "flce_backward", "flce_timing_enable",
+            "flce_timing_collect", "flce_status_string", "flce_last_error", "flce_version"]
 
 
 class Plan(ctypes.Structure):
@@ -44,6 +44,13 @@ class Plan(ctypes.Structure):
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class KernelTime(ctypes.Structure):
+    """Mirror of flce_kernel_time_t."""
+    _fields_ = [("name", ctypes.c_char * 24), ("launches", ctypes.c_int64),
+                ("total_ms", ctypes.c_double), ("flops", ctypes.c_double),
+                ("bytes", ctypes.c_double)]
 
 
 class FlceError(RuntimeError):
@@ -72,6 +79,11 @@ def load(path: str = LIB_PATH):
     lib.flce_forward.restype = ctypes.c_int
     lib.flce_backward.argtypes = [P, vp, vp, vp, vp, i64, f32, vp, vp, ctypes.c_int, vp, u64, vp]
     lib.flce_backward.restype = ctypes.c_int
+    lib.flce_timing_enable.argtypes = [ctypes.c_int]
+    lib.flce_timing_enable.restype = ctypes.c_int
+    lib.flce_timing_collect.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int,
+                                        ctypes.POINTER(ctypes.c_int)]
+    lib.flce_timing_collect.restype = ctypes.c_int
     lib.flce_status_string.argtypes = [ctypes.c_int]
     lib.flce_status_string.restype = ctypes.c_char_p
     lib.flce_last_error.argtypes = []
@@ -124,6 +136,21 @@ def _dtype_code(dtype) -> int:
     if dtype in (torch.float32, "f32", FLCE_F32):
         return FLCE_F32
     raise ValueError(f"unsupported dtype {dtype}")
+
+
+def flce_timing_enable(enable: bool = True) -> None:
+    """flce_timing_enable(): bracket every library launch with hipEvents."""
+    _check(load().flce_timing_enable(1 if enable else 0))
+
+
+def flce_timing_collect() -> dict:
+    """flce_timing_collect(): {kernel: dict(launches, total_ms, flops, bytes)}; clears."""
+    buf = (KernelTime * 16)()
+    n = ctypes.c_int(0)
+    _check(load().flce_timing_collect(buf, 16, ctypes.byref(n)))
+    return {buf[i].name.decode(): dict(launches=buf[i].launches, total_ms=buf[i].total_ms,
+                                       flops=buf[i].flops, bytes=buf[i].bytes)
+            for i in range(n.value)}
 
 
 def flce_plan(T: int, d: int, V: int, dtype, vocab_ws_cap_bytes: int = 0) -> Plan:

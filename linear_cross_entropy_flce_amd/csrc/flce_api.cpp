@@ -9,6 +9,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+#include <vector>
+
 #include "../../include/flce.h"
 #include "flce_launch.h"
 
@@ -50,9 +53,111 @@ flce_status_t hip_fail(hipError_t e, const char* what) {
   return fail(FLCE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// ------------------------------------------------------------ kernel timing
+enum KernelId { K_FWD_SWEEP, K_FWD_MERGE, K_LOSS_SUM, K_BWD_DZ, K_BWD_DH, K_BWD_DW, K_FILL, K_COUNT };
+const char* const kKernelNames[K_COUNT] = {"fwd_sweep", "fwd_merge", "loss_sum", "bwd_dz",
+                                           "bwd_dh",    "bwd_dw",    "fill_zero"};
+
+struct TimingRec {
+  int kid;
+  double flops, bytes;
+  hipEvent_t start, stop;
+};
+
+struct Timing {
+  std::mutex mu;
+  bool enabled = false;
+  std::vector<TimingRec> recs;
+  std::vector<hipEvent_t> pool;
+};
+
+Timing& timing() {
+  static Timing t;
+  return t;
+}
+
+hipEvent_t pooled_event(Timing& t) {
+  if (!t.pool.empty()) {
+    hipEvent_t e = t.pool.back();
+    t.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Brackets one launch with events when timing is enabled.
+class Timed {
+ public:
+  Timed(hipStream_t s, KernelId kid, double flops, double bytes) : s_(s) {
+    Timing& t = timing();
+    std::lock_guard<std::mutex> g(t.mu);
+    if (!t.enabled) return;
+    rec_.kid = kid;
+    rec_.flops = flops;
+    rec_.bytes = bytes;
+    rec_.start = pooled_event(t);
+    rec_.stop = pooled_event(t);
+    if (rec_.start && rec_.stop && hipEventRecord(rec_.start, s_) == hipSuccess) on_ = true;
+  }
+  void done() {
+    if (!on_) return;
+    on_ = false;
+    Timing& t = timing();
+    std::lock_guard<std::mutex> g(t.mu);
+    if (hipEventRecord(rec_.stop, s_) == hipSuccess) t.recs.push_back(rec_);
+  }
+  ~Timed() { done(); }
+
+ private:
+  hipStream_t s_;
+  bool on_ = false;
+  TimingRec rec_{};
+};
+
 }  // namespace
 
 extern "C" {
+
+flce_status_t flce_timing_enable(int enable) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  t.enabled = enable != 0;
+  return ok();
+}
+
+flce_status_t flce_timing_collect(flce_kernel_time_t* out, int max_entries, int* n_out) {
+  if (!out || !n_out) return fail(FLCE_ERR_INVALID_ARG, "out and n_out must be non-NULL");
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  flce_kernel_time_t acc[K_COUNT];
+  memset(acc, 0, sizeof acc);
+  flce_status_t st = FLCE_OK;
+  for (const TimingRec& r : t.recs) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess && st == FLCE_OK) st = hip_fail(e, "timing event");
+    acc[r.kid].launches += 1;
+    acc[r.kid].total_ms += ms;
+    acc[r.kid].flops += r.flops;
+    acc[r.kid].bytes += r.bytes;
+    t.pool.push_back(r.start);
+    t.pool.push_back(r.stop);
+  }
+  t.recs.clear();
+  int n = 0;
+  for (int k = 0; k < K_COUNT && n < max_entries; ++k) {
+    if (acc[k].launches == 0) continue;
+    out[n] = acc[k];
+    snprintf(out[n].name, sizeof out[n].name, "%s", kKernelNames[k]);
+    ++n;
+  }
+  *n_out = n;
+  return st == FLCE_OK ? ok() : st;
+}
+
 
 const char* flce_version(void) { return "0.1.0"; }
 
@@ -174,7 +279,9 @@ flce_status_t flce_forward(const flce_plan_t* plan, const void* H, const void* W
   hipError_t e;
   if (p.T == 0) {
     if (loss_reduced) {
+      Timed tm(s, K_LOSS_SUM, 0, 4);
       e = flce::launch_loss_sum(loss, 0, scale, loss_reduced, s);
+      tm.done();
       if (e != hipSuccess) return hip_fail(e, "loss_sum launch");
     }
     return ok();
@@ -200,7 +307,11 @@ flce_status_t flce_forward(const flce_plan_t* plan, const void* H, const void* W
   const int64_t per_group = (int64_t)a.grp * a.splits;
   const int64_t groups = cdiv(a.n_ttiles, a.grp);
   const int64_t grid = 8 * per_group * cdiv(groups, 8);
+  const double esz = (double)p.elem_bytes;
+  Timed t_sweep(s, K_FWD_SWEEP, 2.0 * p.T * p.d * p.V,
+                (p.T + p.V) * p.d * esz + (double)p.fwd_splits * p.T * 8 + p.T * 12.0);
   e = flce::launch_fwd_sweep(a, bf16, (int)grid, s);
+  t_sweep.done();
   if (e != hipSuccess) return hip_fail(e, "forward sweep launch");
   flce::MergeArgs m;
   m.part = part;
@@ -212,10 +323,14 @@ flce_status_t flce_forward(const flce_plan_t* plan, const void* H, const void* W
   m.splits = p.fwd_splits;
   m.loss = loss;
   m.lse = lse;
+  Timed t_merge(s, K_FWD_MERGE, 0, (double)p.fwd_splits * p.T * 8 + p.T * 20.0);
   e = flce::launch_fwd_merge(m, s);
+  t_merge.done();
   if (e != hipSuccess) return hip_fail(e, "forward merge launch");
   if (loss_reduced) {
+    Timed tm(s, K_LOSS_SUM, 0, p.T * 4.0 + 4);
     e = flce::launch_loss_sum(loss, p.T, scale, loss_reduced, s);
+    tm.done();
     if (e != hipSuccess) return hip_fail(e, "loss_sum launch");
   }
   return ok();
@@ -242,7 +357,9 @@ flce_status_t flce_backward(const flce_plan_t* plan, const void* H, const void* 
   hipError_t e;
   if (p.T == 0) {
     if (!accumulate_dW) {
+      Timed tm(s, K_FILL, 0, p.V * p.d * 4.0);
       e = flce::launch_fill_zero(dW, p.V * p.d, s);
+      tm.done();
       if (e != hipSuccess) return hip_fail(e, "dW fill launch");
     }
     return ok();
@@ -276,7 +393,11 @@ flce_status_t flce_backward(const flce_plan_t* plan, const void* H, const void* 
       z.ldz_cols = (int64_t)z.n_vtiles * ti.logit_bm;
       z.grad_scale = grad_scale;
       z.dz = dz;
+      const double esz = (double)p.elem_bytes;
+      const double tc = t_count, vc = v_count, dd = (double)p.d;
+      Timed t_dz(s, K_BWD_DZ, 2.0 * tc * dd * vc, (tc + vc) * dd * esz + tc * 12 + tc * vc * esz);
       e = flce::launch_bwd_dz(z, bf16, s);
+      t_dz.done();
       if (e != hipSuccess) return hip_fail(e, "dZ launch");
 
       flce::DhArgs h;
@@ -297,7 +418,12 @@ flce_status_t flce_backward(const flce_plan_t* plan, const void* H, const void* 
       else h.mode = 2;
       h.dh_acc = dh_acc;
       h.dH = dH;
+      Timed t_dh(s, K_BWD_DH, 2.0 * tc * dd * vc,
+                 tc * vc * esz + vc * dd * esz +
+                     tc * dd * (h.mode == 1 || h.mode == 2 ? 4.0 : 0.0) +
+                     tc * dd * (h.mode >= 2 ? esz : 4.0));
       e = flce::launch_bwd_dh(h, bf16, s);
+      t_dh.done();
       if (e != hipSuccess) return hip_fail(e, "dH launch");
 
       flce::DwArgs w;
@@ -314,7 +440,10 @@ flce_status_t flce_backward(const flce_plan_t* plan, const void* H, const void* 
       w.n_ntiles = (int)cdiv(p.d, ti.dw_bn);
       w.accumulate = (b > 0 || accumulate_dW) ? 1 : 0;
       w.dW = dW;
+      Timed t_dw(s, K_BWD_DW, 2.0 * tc * dd * vc,
+                 tc * vc * esz + tc * dd * esz + vc * dd * (w.accumulate ? 8.0 : 4.0));
       e = flce::launch_bwd_dw(w, bf16, s);
+      t_dw.done();
       if (e != hipSuccess) return hip_fail(e, "dW launch");
     }
   }

@@ -198,10 +198,12 @@ struct Tile {
       c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
     } else {
+      // bit-cast whole vectors: a bit cast of a vector element (a[q]) reads
+      // element 0 with this compiler
+      const f32x4_t af = __builtin_bit_cast(f32x4_t, a);
+      const f32x4_t bf = __builtin_bit_cast(f32x4_t, b);
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a[q]),
-                                                 __builtin_bit_cast(float, b[q]), c, 0, 0, 0);
+      for (int q = 0; q < 4; ++q) c = __builtin_amdgcn_mfma_f32_32x32x2f32(af[q], bf[q], c, 0, 0, 0);
     }
   }
 

@@ -103,12 +103,24 @@ def test_large_logits_running_max():
         got = run_gpu(inp)
         ref = _ref(inp, 1.0)
         assert np.all(np.isfinite(got["loss"])) and np.all(np.isfinite(got["lse"]))
-        # loss tolerance scales with the ulp of |lse| (float32 arithmetic)
-        tl = TOL[dtype]["loss"] + 4 * np.abs(ref["lse"]).max() * 2.0 ** -23
+        # float32 logits near |lse| carry an absolute error of a few ulp(|lse|):
+        # the loss tolerance grows by that much
+        ulp = np.abs(ref["lse"]).max() * 2.0 ** -23
+        tl = TOL[dtype]["loss"] + 4 * ulp
         assert max_abs(got["loss"], ref["loss"]) <= tl
         assert max_abs(got["lse"], ref["lse"]) <= tl
-        assert rel_fro(got["dH"], ref["dH"]) <= 2 * TOL[dtype]["grad"]
-        assert rel_fro(got["dW"], ref["dW"]) <= 2 * TOL[dtype]["grad"]
+        # the same absolute error in z - lse is a relative error of every
+        # softmax entry, hence of dZ
+        tg = TOL[dtype]["grad"] + 8 * ulp
+        assert rel_fro(got["dW"], ref["dW"]) <= tg
+        assert rel_fro(got["dH"][:, 1:], ref["dH"][:, 1:]) <= tg
+        # column 0 of dH is sum_j dZ_ij (w_j0 + c0): the c0 part is zero in exact
+        # arithmetic (dZ rows sum to 0) but carries c0 times the rounding of dZ,
+        # whose row sums of magnitudes are at most 2 (grad scale 1); bf16 dZ
+        # storage rounds to 2^-9 relative
+        u = (2.0 ** -8 if dtype == wl.DTYPE_BF16 else 0.0) + 8 * ulp
+        bound = 2 * c[0] * u + tg * np.abs(ref["dH"][:, 0]).max()
+        assert max_abs(got["dH"][:, 0], ref["dH"][:, 0]) <= bound
 
 
 @pytest.mark.parametrize("dtype", [wl.DTYPE_F32, wl.DTYPE_BF16])
@@ -118,7 +130,9 @@ def test_several_blocks_and_slabs(dtype):
     T, d, V = 1100, 96, 3000
     inp = wl.make_inputs(T, d, V, dtype, seed=17, sigma_w=0.4, ignore_frac=0.1)
     esz = 4 if dtype == wl.DTYPE_F32 else 2
-    cap = 512 * 1024 * esz + 512 * d * 4
+    tile_v = 128 if dtype == wl.DTYPE_F32 else 256
+    # room for a 512-token block, its fp32 dH accumulator and one vocab tile
+    cap = 512 * (d * 4 + tile_v * esz)
     got = run_gpu(inp, grad_scale=0.25, cap=cap)
     plan = got["plan"]
     log("plan", plan.n_blocks, plan.n_slabs, plan.bwd_block, plan.bwd_slab)
