@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Fused linear cross-entropy forward + backward on one MI355X.
+
+One step = flce_forward (per-token loss and lse) + flce_backward (dH, dW) over
+one synthetic batch of the pages' per-rank shape: T = 65,536 tokens,
+d = 2,048, V = 124,160, bf16 inputs, uniform targets, no ignored tokens,
+grad scale 1 (no reduction).  Inputs are resident in HBM before the timed
+region starts.
+
+Prints ONE JSON line on stdout:
+  value   = counted TFLOP/s = 8*T*d*V per step / step time (forward 2TdV,
+            backward 6TdV including the logit recompute)
+  roofline = the kernel with the largest share of the timed region, its
+            algorithmic flops per launch over its average launch time,
+            measured with hipEvents on the launch stream, against the
+            2.5 PFLOP/s dense bf16 MFMA peak
+  cpu_baseline = the CPU oracle (numpy float64) timed on a bounded sample of
+            the same workload on this host's cores
+
+Progress goes to stderr.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused linear-CE fwd+bwd TFLOP/s (8·T·d·V) and % MFMA peak at T=64K,V=124,160"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(inp, cfg, n_rows: int):
+    """The oracle as it stands, on n_rows seeded rows of the workload: loss,
+    lse, dH and the rows' dW contribution, i.e. the whole step for those rows."""
+    import numpy as np
+
+    import oracle
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: report the core count
+        threads = os.cpu_count() or 1
+    rows = wl.sample_rows(cfg, n_rows)
+    Hs = inp.H_f32()[rows]
+    Wf = inp.W_f32()
+    ys = inp.y[rows]
+    ls, gs = cfg.scales()
+    t0 = time.perf_counter()
+    oracle.forward_backward(Hs, Wf, ys, wl.IGNORE_INDEX, gs, row_chunk=256)
+    dt = time.perf_counter() - t0
+    counted = 8.0 * n_rows * cfg.d * cfg.V
+    return {"value": counted / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n_rows} seeded token rows of the same workload (all {cfg.V} vocab "
+                      f"columns, d={cfg.d}): numpy float64 logits, lse, loss, dH and the rows' dW; "
+                      f"{dt:.2f} s; counted as 8*rows*d*V like the GPU figure",
+            "seconds": dt, "host_cpus": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, help="workload index (default 3)")
+    ap.add_argument("--cpu-rows", type=int, default=2048,
+                    help="rows of the CPU-oracle sample (0 skips it)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one MI355X only: the fused linear cross-entropy path here is the "
+              "single-GPU kernel set (no collectives).  Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import linear_cross_entropy_flce_amd as flce
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(3)
+    flce.load()
+    cfg = wl.CONFIGS[args.config]
+    log(f"workload {cfg.name}: generating inputs")
+    t0 = time.perf_counter()
+    inp = wl.config_inputs(cfg)
+    log(f"  inputs ready in {time.perf_counter() - t0:.1f} s")
+    dev = torch.device("cuda:0")
+    bf16 = cfg.dtype == wl.DTYPE_BF16
+    if bf16:
+        H = torch.from_numpy(inp.H.view(np.int16)).to(dev).view(torch.bfloat16)
+        W = torch.from_numpy(inp.W.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        H = torch.from_numpy(inp.H).to(dev)
+        W = torch.from_numpy(inp.W).to(dev)
+    y = torch.from_numpy(inp.y).to(dev)
+    T, d, V = cfg.T, cfg.d, cfg.V
+    ls, gs = cfg.scales()
+    plan = flce.flce_plan(T, d, V, cfg.dtype)
+    ws = flce.workspace(plan, dev)
+    loss = torch.empty(T, dtype=torch.float32, device=dev)
+    lse = torch.empty(T, dtype=torch.float32, device=dev)
+    dH = torch.empty((T, d), dtype=H.dtype, device=dev)
+    dW = torch.empty((V, d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        flce.flce_forward(plan, H, W, y, wl.IGNORE_INDEX, ls, loss=loss, lse=lse, ws=ws,
+                          stream=stream)
+        flce.flce_backward(plan, H, W, y, lse, wl.IGNORE_INDEX, gs, dH=dH, dW=dW, ws=ws,
+                           stream=stream)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    flce.flce_timing_collect()  # discard anything recorded so far
+    flce.flce_timing_enable(True)
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    flce.flce_timing_enable(False)
+    kernels = flce.flce_timing_collect()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    peak_mem = torch.cuda.max_memory_allocated()
+    counted = 8.0 * T * d * V
+    value = counted / (ms / 1e3) / 1e12
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
+    log(f"  {ms:.2f} ms/step (wall {wall / args.steps * 1e3:.2f} ms), {value:.1f} TFLOP/s, "
+        f"{100 * value / peak:.1f}% of {peak} TFLOP/s")
+    step_kernel_ms = sum(k["total_ms"] for k in kernels.values()) / args.steps
+    for name, k in kernels.items():
+        tf = k["flops"] / (k["total_ms"] / 1e3) / 1e12 if k["total_ms"] else 0.0
+        log(f"  {name:10s} launches {k['launches']:5d}  avg {k['total_ms'] / k['launches']:8.3f} ms"
+            f"  share {k['total_ms'] / args.steps / ms:6.1%}  {tf:7.1f} TFLOP/s")
+    dom_name, dom = max(kernels.items(), key=lambda kv: kv[1]["total_ms"])
+    avg_ms = dom["total_ms"] / dom["launches"]
+    flops_per_launch = dom["flops"] / dom["launches"]
+    achieved = flops_per_launch / (avg_ms / 1e3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom_name, "achieved": round(achieved, 2),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": None, "flops_per_launch": flops_per_launch,
+                "avg_launch_ms": round(avg_ms, 4), "launches": dom["launches"]}
+
+    cpu = None
+    if args.cpu_rows > 0:
+        log(f"cpu baseline: oracle on {args.cpu_rows} rows")
+        cpu = cpu_baseline(inp, cfg, args.cpu_rows)
+        log(f"  {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads ({cpu['seconds']:.1f} s)")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": T, "d": d, "V": V, "precision": cfg.dtype,
+                   "targets": cfg.targets, "ignored_tokens": cfg.n_ignored,
+                   "grad_scale": gs, "parallelism": "single GPU"},
+        "mfma_peak_frac": round(value / peak, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "memory": {"peak_allocated_bytes": int(peak_mem),
+                   "workspace_bytes": int(plan.ws_bytes),
+                   "vocab_axis_workspace_bytes": int(plan.dz_ws_bytes),
+                   "naive_logits_one_copy_bytes": int(plan.naive_logits_bytes),
+                   "naive_logits_and_grad_bytes": int(2 * plan.naive_logits_bytes)},
+        "kernels": {k: {"launches": v["launches"], "avg_ms": round(v["total_ms"] / v["launches"], 4),
+                        "share": round(v["total_ms"] / args.steps / ms, 4),
+                        "tflops": round(v["flops"] / (v["total_ms"] / 1e3) / 1e12, 2)
+                        if v["total_ms"] else 0.0}
+                    for k, v in kernels.items()},
+        "kernel_ms_per_step": round(step_kernel_ms, 3),
+        "plan": {"fwd_splits": plan.fwd_splits, "bwd_block": plan.bwd_block,
+                 "bwd_slab": plan.bwd_slab, "n_blocks": plan.n_blocks, "n_slabs": plan.n_slabs},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

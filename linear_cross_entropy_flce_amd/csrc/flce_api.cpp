@@ -22,6 +22,7 @@ constexpr uint64_t kDefaultCap = 950000000ull;
 constexpr uint64_t kMaxCap = 0x7fff0000ull;
 constexpr int64_t kMaxBlock = 8192;
 constexpr int kTargetWorkgroups = 256;  // one per compute unit
+constexpr int64_t kComputeUnits = 256;  // MI355X
 
 thread_local char g_err[512] = "";
 
@@ -115,6 +116,34 @@ class Timed {
   bool on_ = false;
   TimingRec rec_{};
 };
+
+// Modelled time of the backward pass for token block B and vocab slab Vs, in
+// units of one 256 x 256 x 256 MFMA block per compute unit.  Every launch
+// runs whole rounds of kComputeUnits workgroups, so a grid of n tiles costs
+// ceil(n / CU) rounds; the recompute tile also pays its exp/store epilogue,
+// the dW tile its fp32 read-modify-write, and each slab a dH accumulator pass.
+double backward_cost(int64_t T, int64_t d, int64_t V, int64_t B, int64_t Vs,
+                     const flce::TileInfo& ti) {
+  const double unit = 256.0 * 256.0 * 256.0;
+  const int64_t n_dt_h = cdiv(d, ti.dh_bn), n_dt_w = cdiv(d, ti.dw_bn);
+  double cost = 0;
+  for (int64_t t0 = 0; t0 < T; t0 += B) {
+    const int64_t tc = T - t0 < B ? T - t0 : B;
+    for (int64_t v0 = 0; v0 < V; v0 += Vs) {
+      const int64_t vc = V - v0 < Vs ? V - v0 : Vs;
+      const int64_t dz_tiles = cdiv(vc, ti.logit_bm) * cdiv(tc, ti.logit_bn);
+      const int64_t dh_tiles = cdiv(tc, ti.dh_bm) * n_dt_h;
+      const int64_t dw_tiles = cdiv(vc, ti.dw_bm) * n_dt_w;
+      const double dz_tile = (double)ti.logit_bm * ti.logit_bn * d / unit;
+      const double dh_tile = (double)ti.dh_bm * ti.dh_bn * vc / unit;
+      const double dw_tile = (double)ti.dw_bm * ti.dw_bn * tc / unit;
+      cost += cdiv(dz_tiles, kComputeUnits) * dz_tile * 1.10;
+      cost += cdiv(dh_tiles, kComputeUnits) * (dh_tile + 0.5);
+      cost += cdiv(dw_tiles, kComputeUnits) * dw_tile * (t0 > 0 ? 1.07 : 1.035);
+    }
+  }
+  return cost;
+}
 
 }  // namespace
 
@@ -217,29 +246,28 @@ flce_status_t flce_plan(int64_t T, int64_t d, int64_t V, flce_dtype_t dtype, uin
   p.fwd_tiles_per_split = (int32_t)tps;
   p.fwd_ws_bytes = (uint64_t)round_up(splits * T * 2 * 4, 256) + (uint64_t)round_up(T * 4, 256);
 
-  // ---- backward: largest token block (<= 8192, tile multiple) whose dZ
-  // buffer (plus fp32 dH accumulator when the vocab needs several slabs)
-  // fits under the cap.
+  // ---- backward: the largest token block B (<= 8192, tile multiple) for
+  // which some vocab slab fits under the cap, then the slab width that
+  // minimises the modelled time (backward_cost): a dZ buffer of B x Vs plus
+  // the fp32 dH accumulator when the vocab needs several slabs.
   const int64_t Tr = round_up(T > 0 ? T : 1, ti.logit_bn);
   const int64_t Vfull = round_up(V, ti.logit_bm);
   int64_t best_B = 0, best_Vs = 0, best_slabs = 0;
-  for (int64_t B = (Tr < kMaxBlock ? Tr : kMaxBlock); B >= ti.logit_bn; B -= ti.logit_bn) {
-    if ((uint64_t)(B * Vfull * esz) <= cap) {
-      best_B = B;
-      best_Vs = Vfull;
-      best_slabs = 1;
-      break;
+  for (int64_t B = (Tr < kMaxBlock ? Tr : kMaxBlock); B >= ti.logit_bn && best_B == 0;
+       B -= ti.logit_bn) {
+    double best_cost = 0;
+    for (int64_t Vs = ti.logit_bm; Vs <= Vfull; Vs += ti.logit_bm) {
+      const int64_t slabs = cdiv(V, Vs);
+      const uint64_t need = (uint64_t)(B * Vs * esz) + (slabs > 1 ? (uint64_t)(B * d * 4) : 0);
+      if (need > cap) break;  // need grows with Vs
+      const double c = backward_cost(T > 0 ? T : 1, d, V, B, Vs, ti);
+      if (best_B == 0 || c < best_cost * (1 - 1e-9)) {
+        best_cost = c;
+        best_B = B;
+        best_Vs = Vs;
+        best_slabs = slabs;
+      }
     }
-    const int64_t acc = B * d * 4;
-    if ((uint64_t)acc >= cap) continue;
-    const int64_t avail = (int64_t)cap - acc;
-    const int64_t vs_max = (avail / (B * esz)) / ti.logit_bm * ti.logit_bm;
-    if (vs_max < ti.logit_bm) continue;
-    const int64_t slabs = cdiv(Vfull, vs_max);
-    best_B = B;
-    best_Vs = round_up(cdiv(Vfull, slabs), ti.logit_bm);
-    best_slabs = cdiv(V, best_Vs);
-    break;
   }
   if (best_B == 0)
     return fail(FLCE_ERR_WORKSPACE,

@@ -32,40 +32,74 @@ constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Logits tiles: 256 vocab x 256 tokens, 2 x 4 waves of 128 x 64 (bf16);
-// 128 x 128 with 2 x 2 waves of 64 x 64 for fp32.
+// Argument of exp2 for exp(z - m).  bf16 inputs: one FMA, z * log2(e) + nb with
+// nb = -m * log2(e); its rounding error (|z| * 2^-24 relative to the exponent)
+// is far below bf16 input precision.  fp32 inputs: subtract first, so the
+// exponent error stays at the rounding of (z - m).
+template <int ESZ>
+__device__ __forceinline__ float exp2_arg(float z, float m, float nb) {
+  if constexpr (ESZ == 2) return fmaf(z, kLog2e, nb);
+  else return (z - m) * kLog2e;
+}
+// Same for g * exp(z - lse) with log2|g| folded in (bias = log2|g| - lse * log2(e),
+// or +-inf / NaN for ignored / invalid targets, which the fp32 form keeps).
+template <int ESZ>
+__device__ __forceinline__ float dz_arg(float z, float lse, float log2g, float bias) {
+  if constexpr (ESZ == 2) return fmaf(z, kLog2e, bias);
+  else return (bias != bias || bias == kNegInf) ? bias : fmaf(z - lse, kLog2e, log2g);
+}
+
+// Tile shapes: 256 x 256 per workgroup in 2 x 4 waves of 128 x 64 (bf16);
+// 128 x 128 in 2 x 2 waves of 64 x 64 for fp32.  Each kernel picks its
+// global -> LDS path (DMA ring of NS stages with 64-byte k rows, or the
+// register-staged double buffer with 128-byte k rows) by measurement.
+#ifndef FLCE_LOGIT_NS
+#define FLCE_LOGIT_NS 2
+#endif
+#ifndef FLCE_DH_NS
+#define FLCE_DH_NS 2
+#endif
+#ifndef FLCE_DW_NS
+#define FLCE_DW_NS 2
+#endif
+template <typename E, bool A_KC, bool B_KC, int NS>
+using BigTile = Tile<256, 256, 2, 4, E, A_KC, B_KC, NS == 2 ? 128 : 64, NS, NS != 2>;
+template <typename E, bool A_KC, bool B_KC, int NS>
+using SmallTile = Tile<128, 128, 2, 2, E, A_KC, B_KC, NS == 2 ? 128 : 64, NS, NS != 2>;
+
+// Logits (A = W rows, B = H rows, both K-contiguous).
 template <typename E>
 struct LogitCfg;
 template <>
 struct LogitCfg<__bf16> {
-  using T = Tile<256, 256, 2, 4, __bf16, true, true>;
+  using T = BigTile<__bf16, true, true, FLCE_LOGIT_NS>;
 };
 template <>
 struct LogitCfg<float> {
-  using T = Tile<128, 128, 2, 2, float, true, true>;
+  using T = SmallTile<float, true, true, FLCE_LOGIT_NS>;
 };
 
-// Contraction tiles for dH (A = dZ K-contiguous, B = W MN-contiguous) and dW
-// (A = dZ MN-contiguous, B = H MN-contiguous).
+// dH (A = dZ K-contiguous, B = W MN-contiguous) and dW (A = dZ MN-contiguous,
+// B = H MN-contiguous).
 template <typename E>
 struct DhCfg;
 template <>
 struct DhCfg<__bf16> {
-  using T = Tile<256, 256, 2, 4, __bf16, true, false>;
+  using T = BigTile<__bf16, true, false, FLCE_DH_NS>;
 };
 template <>
 struct DhCfg<float> {
-  using T = Tile<128, 128, 2, 2, float, true, false>;
+  using T = SmallTile<float, true, false, FLCE_DH_NS>;
 };
 template <typename E>
 struct DwCfg;
 template <>
 struct DwCfg<__bf16> {
-  using T = Tile<256, 256, 2, 4, __bf16, false, false>;
+  using T = BigTile<__bf16, false, false, FLCE_DW_NS>;
 };
 template <>
 struct DwCfg<float> {
-  using T = Tile<128, 128, 2, 2, float, false, false>;
+  using T = SmallTile<float, false, false, FLCE_DW_NS>;
 };
 
 __device__ __forceinline__ uint32_t clamp_bytes(int64_t b) {
@@ -167,11 +201,12 @@ __global__ void __launch_bounds__(LogitCfg<E>::T::NT, 1)
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, tile.acc[i][j][r]);
       const float m_new = fmaxf(m_run[j], mx);
       if (m_new != kNegInf) {
+        const float nb = -m_new * kLog2e;
         float sum = 0.f;
 #pragma unroll
         for (int i = 0; i < TL::MI; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sum += fast_exp2((tile.acc[i][j][r] - m_new) * kLog2e);
+          for (int r = 0; r < 16; ++r) sum += fast_exp2(exp2_arg<TL::ESZ>(tile.acc[i][j][r], m_new, nb));
         s_run[j] = s_run[j] * fast_exp2((m_run[j] - m_new) * kLog2e) + sum;
         m_run[j] = m_new;
       }
@@ -319,40 +354,71 @@ __global__ void __launch_bounds__(LogitCfg<E>::T::NT, 1) bwd_dz_kernel(DzArgs a)
   tile.zero();
   if (A.rows > 0) tile.mainloop(A, B, a.d, lds);
 
+  // dZ = g * exp(z - lse) - g * [row == target]: with |g| folded into the
+  // exponent, each element costs one FMA and one exp2:
+  //   g * exp(z - lse) = sign(g) * exp2(z * log2(e) + (log2|g| - lse * log2(e))).
+  // Ignored tokens get a -inf bias (exactly 0), invalid targets a NaN bias.
   const float g = a.grad_scale;
+  const float gsign = g < 0.f ? -1.f : 1.f;
+  const float log2g = g == 0.f ? kNegInf : __log2f(fabsf(g));
+  const bool tail = v0 + TL::BM > a.V;  // last vocab tile: rows past V are zero
+  const int lim = a.V - (int)v0 - wm * TL::WTM - 4 * (lane >> 5);
   E* dz = reinterpret_cast<E*>(a.dz);
 #pragma unroll
   for (int j = 0; j < TL::NI; ++j) {
     const int c = TL::col_of(wn, j);
     const int64_t tl = tl0 + c;
-    if (tl >= a.t_count) continue;
-    const int64_t t = a.t_begin + tl;
+    const bool col_ok = tl < a.t_count;
+    const int64_t t = a.t_begin + (col_ok ? tl : 0);
     const int code = target_code(a.y, t, a.ignore_index, a.V);
-    const float lse = a.lse[t];
-    const float scale = code == -1 ? 0.f : (code == -2 ? __builtin_nanf("") : g);
-    const int rt = code - (int)v0;  // target row within the workgroup tile
+    const float lse_t = a.lse[t];
+    const float bias = code == -1 ? kNegInf
+                       : code == -2 ? __builtin_nanf("")
+                                    : log2g - lse_t * kLog2e;
+    // the sign of g is uniform: two copies of the loop keep it out of the
+    // per-element work
+    if (gsign > 0.f) {
+#pragma unroll
+      for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          tile.acc[i][j][r] = fast_exp2(dz_arg<TL::ESZ>(tile.acc[i][j][r], lse_t, log2g, bias));
+    } else {
+#pragma unroll
+      for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          tile.acc[i][j][r] = -fast_exp2(dz_arg<TL::ESZ>(tile.acc[i][j][r], lse_t, log2g, bias));
+    }
+    // the one-hot term (rare: only the wave holding the target row)
+    const int wrow0 = (int)v0 + wm * TL::WTM;
+    if (code >= wrow0 && code < wrow0 + TL::WTM) {
+      const int rt = code - wrow0 - 4 * (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (rt == i * 32 + 8 * (r >> 2) + (r & 3)) tile.acc[i][j][r] -= g;
+    }
+    if (tail) {
+#pragma unroll
+      for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (i * 32 + 8 * (r >> 2) + (r & 3) >= lim) tile.acc[i][j][r] = 0.f;
+    }
+    if (!col_ok) continue;
 #pragma unroll
     for (int i = 0; i < TL::MI; ++i)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        float o[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int r = rq * 4 + u;
-          const int row = TL::row_of(wm, i, r);
-          float p = fast_exp2((tile.acc[i][j][r] - lse) * kLog2e);
-          float val = scale * p;
-          if (row == rt) val -= scale;
-          if (v0 + row >= a.V) val = 0.f;
-          o[u] = val;
-        }
         const int row0 = TL::row_of(wm, i, rq * 4);
         const int64_t vl = v0 - a.v_begin + row0;  // vocab within the slab
         if (vl < a.ldz_cols)
-          store4<E>(dz + tl * a.ldz + vl, o[0], o[1], o[2], o[3]);
+          store4<E>(dz + tl * a.ldz + vl, tile.acc[i][j][rq * 4], tile.acc[i][j][rq * 4 + 1],
+                    tile.acc[i][j][rq * 4 + 2], tile.acc[i][j][rq * 4 + 3]);
       }
   }
-  (void)lane;
 }
 
 // ================================================================ backward dH

@@ -11,11 +11,12 @@
 // (both KC), while dH = dZ W contracts W over the vocab axis and
 // dW = dZ^T H contracts H and dZ over the token axis (MC).
 //
-// Global -> LDS: each thread moves 16-byte chunks through registers, one
-// k-tile ahead of the MFMA work (LDS double buffer, one barrier per k-tile).
-//   KC tiles are stored [row][128 bytes of k] with the 16-byte chunk index
-//   XOR-swizzled by (row & 7) so that the 32 lanes reading one MFMA fragment
-//   column hit distinct banks.
+// Global -> LDS: direct DMA (buffer_load_dwordx4 ... lds), no register
+// staging, into a ring of NS stages that runs NS - 1 stages ahead of the MFMA
+// work (one barrier per stage).
+//   KC tiles are stored [row][KB bytes of k] with the 16-byte chunk index
+//   XOR-swizzled so that the lanes reading one MFMA fragment column hit
+//   distinct banks.
 //   MC tiles are stored [k][row] with a 64-byte row pad, and fragments are read
 //   with ds_read_b64_tr_b16 (bf16), the gfx950 LDS transpose read: within each
 //   16-lane group, lanes 4s..4s+3 fetch 16 consecutive elements of one LDS row
@@ -78,30 +79,44 @@ struct ElemTraits<float> {
   static constexpr int kBytes = 4;
 };
 
-template <int BM_, int BN_, int WM_, int WN_, typename E, bool A_KC, bool B_KC>
+template <int BM_, int BN_, int WM_, int WN_, typename E, bool A_KC, bool B_KC, int KB_ = 64,
+          int NS_ = 3, bool DMA_ = true>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-  static constexpr int NT = WM * WN * 64;       // threads per workgroup
+  static constexpr int NW = WM * WN;             // waves per workgroup
+  static constexpr int NT = NW * 64;             // threads per workgroup
   static constexpr int ESZ = ElemTraits<E>::kBytes;
-  static constexpr int CW = 16 / ESZ;           // elements per 16-byte chunk
-  static constexpr int BK = 128 / ESZ;          // k per LDS stage (128 bytes)
-  static constexpr int KSTEP = 2 * CW;          // k per fragment step
+  static constexpr int CW = 16 / ESZ;            // elements per 16-byte chunk
+  static constexpr int KB = KB_;                 // bytes of k per KC row per stage
+  static constexpr int NS = NS_;                 // LDS ring stages (2 without DMA)
+  static constexpr bool DMA = DMA_;              // global -> LDS by DMA, else through VGPRs
+  static constexpr int BK = KB / ESZ;            // k per stage
+  static constexpr int KSTEP = 2 * CW;           // k per fragment step
+  static constexpr int KS = BK / KSTEP;          // fragment steps per stage
+  static constexpr int CPR = KB / 16;            // 16-byte chunks per KC row
+  static constexpr int RPB = 1024 / KB;          // KC rows per 1 KB DMA block
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int MI = WTM / 32, NI = WTN / 32;
   static constexpr int A_PITCH = BM * ESZ + 64;  // MC LDS row pitch (bytes)
   static constexpr int B_PITCH = BN * ESZ + 64;
-  static constexpr int A_BYTES = A_KC ? BM * 128 : BK * A_PITCH;
-  static constexpr int B_BYTES = B_KC ? BN * 128 : BK * B_PITCH;
+  static constexpr int A_NB = A_KC ? BM * KB / 1024 : (BK * A_PITCH + 1023) / 1024;  // DMA blocks
+  static constexpr int B_NB = B_KC ? BN * KB / 1024 : (BK * B_PITCH + 1023) / 1024;
+  static constexpr int A_BYTES = A_NB * 1024;
+  static constexpr int B_BYTES = B_NB * 1024;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int LDS_BYTES = 2 * STAGE;
-  static constexpr int A_LD = BM * BK / CW / NT;  // 16-byte loads per thread per stage
-  static constexpr int B_LD = BN * BK / CW / NT;
+  static constexpr int LDS_BYTES = NS * STAGE;
+  static constexpr int A_J = (A_NB + NW - 1) / NW;  // DMA instructions per wave (upper bound)
+  static constexpr int B_J = (B_NB + NW - 1) / NW;
   static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "wave tile must be 32-aligned");
-  static_assert((BM * BK / CW) % NT == 0 && (BN * BK / CW) % NT == 0, "loads must divide");
+  static_assert(KS >= 1 && BK % KSTEP == 0, "stage must hold whole fragment steps");
+  static_assert(KB == 64 || KB == 128, "KC rows of 64 or 128 bytes");
+  static_assert(DMA ? NS >= 3 : NS == 2, "DMA ring of >= 3 stages, or a double buffer");
+  static constexpr int A_LD = BM * BK / CW / NT;  // 16-byte loads per thread per stage (no DMA)
+  static constexpr int B_LD = BN * BK / CW / NT;
+  static_assert(DMA || ((BM * BK / CW) % NT == 0 && (BN * BK / CW) % NT == 0), "loads must divide");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
   f32x16_t acc[MI][NI];
-  u32x4_t ra[A_LD], rb[B_LD];
 
   __device__ __forceinline__ void zero() {
 #pragma unroll
@@ -112,7 +127,73 @@ struct Tile {
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   }
 
-  // ---------------------------------------------------------------- global
+  // Chunk swizzle of the KC layout: the 16 rows read by 16 lanes at one
+  // logical chunk land in 16 distinct 16-byte bank groups of the 64 x 4-byte
+  // LDS banks (256 / KB rows share one bank window).
+  __device__ __forceinline__ static int swz(int row) { return (row / (256 / KB)) % CPR; }
+
+  // ------------------------------------------------------ global -> LDS (DMA)
+  // One buffer_load_dwordx4 ... lds moves 64 x 16 bytes into a contiguous
+  // 1 KB block of LDS (lane l -> byte 16 l).  Each lane picks the global chunk
+  // that belongs at its slot, so the swizzled / padded layouts come for free.
+  // Blocks are dealt round-robin over the waves.
+  struct Dma {
+    uint32_t off[A_J + B_J];  // byte offset from the operand base at k0 = 0
+    int krel[A_J + B_J];      // KC: k of the chunk;  MC: k row within the stage
+    bool ok[A_J + B_J];       // the slot is inside the operand (row / column bounds)
+  };
+
+  template <bool KC, int ROWS, int PITCH, int NB, int J>
+  __device__ __forceinline__ static void dma_setup(const Operand& op, int wave, uint32_t* off,
+                                                   int* krel, bool* ok) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int b = wave + NW * j;
+      if constexpr (KC) {
+        const int row = b * RPB + lane / CPR;
+        const int kc = (lane % CPR) ^ swz(row);
+        off[j] = (uint32_t)row * op.ld_bytes + (uint32_t)kc * 16;
+        krel[j] = kc * CW;
+        ok[j] = b < NB && row < op.rows;
+      } else {
+        const int o = b * 1024 + 16 * lane;
+        const int kr = o / PITCH, cb = o % PITCH;
+        off[j] = (uint32_t)kr * op.ld_bytes + (uint32_t)cb;
+        krel[j] = kr;
+        ok[j] = b < NB && kr < BK && cb < ROWS * ESZ && (cb / 16) * CW < op.cols;
+      }
+    }
+  }
+
+  template <bool KC, int NB, int J>
+  __device__ __forceinline__ static void dma_issue(const Operand& op, __amdgpu_buffer_rsrc_t rs,
+                                                   int wave, int k0, char* dst,
+                                                   const uint32_t* off, const int* krel,
+                                                   const bool* ok) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int b = wave + NW * j;
+      if (J * NW == NB || b < NB) {
+        bool v;
+        uint32_t o;
+        if constexpr (KC) {
+          v = ok[j] && k0 + krel[j] < op.cols;
+          o = off[j] + (uint32_t)k0 * ESZ;
+        } else {
+          v = ok[j] && k0 + krel[j] < op.rows;
+          o = off[j] + (uint32_t)k0 * op.ld_bytes;
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(dst + b * 1024), 16, v ? o : kOOB, 0, 0,
+            0);
+      }
+    }
+  }
+
+  // ------------------------------------------- global -> VGPR -> LDS staging
+  // Thread c of the workgroup moves chunk c, c + NT, ... of the stage: KC rows
+  // are CPR chunks wide, MC rows ROWS * ESZ / 16 chunks.
   template <bool KC, int ROWS, int NLD>
   __device__ __forceinline__ static void gload(const Operand& op, __amdgpu_buffer_rsrc_t rs,
                                                int k0, u32x4_t* r) {
@@ -122,13 +203,13 @@ struct Tile {
       const int c = tid + NT * i;
       uint32_t off;
       if constexpr (KC) {
-        const int row = c >> 3, kc = c & 7;
+        const int row = c / CPR, kc = c % CPR;
         const int k = k0 + kc * CW;
         off = (row < op.rows && k < op.cols) ? (uint32_t)row * op.ld_bytes + (uint32_t)k * ESZ
                                              : kOOB;
       } else {
-        constexpr int CPR = ROWS * ESZ / 16;  // chunks per LDS row
-        const int kr = c / CPR, cc = c % CPR;
+        constexpr int RC = ROWS * ESZ / 16;
+        const int kr = c / RC, cc = c % RC;
         const int k = k0 + kr;
         off = (k < op.rows && cc * CW < op.cols) ? (uint32_t)k * op.ld_bytes + (uint32_t)cc * 16
                                                  : kOOB;
@@ -145,23 +226,23 @@ struct Tile {
       const int c = tid + NT * i;
       int off;
       if constexpr (KC) {
-        const int row = c >> 3, kc = c & 7;
-        off = row * 128 + ((kc ^ (row & 7)) << 4);
+        const int row = c / CPR, kc = c % CPR;
+        off = row * KB + ((kc ^ swz(row)) << 4);
       } else {
-        constexpr int CPR = ROWS * ESZ / 16;
-        off = (c / CPR) * PITCH + (c % CPR) * 16;
+        constexpr int RC = ROWS * ESZ / 16;
+        off = (c / RC) * PITCH + (c % RC) * 16;
       }
       *reinterpret_cast<u32x4_t*>(lds + off) = r[i];
     }
   }
 
   // --------------------------------------------------------------- fragments
-  // KC: lane reads its row's 16-byte chunk (2*ks + half) of the 128-byte k row.
+  // KC: lane reads chunk (2*ks + half) of its row.
   __device__ __forceinline__ static u32x4_t frag_kc(const char* lds, int row0, int ks) {
     const int lane = threadIdx.x & 63;
     const int row = row0 + (lane & 31);
     const int chunk = ks * 2 + (lane >> 5);
-    return *reinterpret_cast<const u32x4_t*>(lds + row * 128 + ((chunk ^ (row & 7)) << 4));
+    return *reinterpret_cast<const u32x4_t*>(lds + row * KB + ((chunk ^ swz(row)) << 4));
   }
 
   // MC, bf16: two transpose reads give k = 16*ks + 8*half + 0..7 of column row0 + lane%32.
@@ -207,60 +288,174 @@ struct Tile {
     }
   }
 
-  __device__ __forceinline__ void compute_stage(const char* la, const char* lb, int wm, int wn) {
+  // Fragments of one k step (KSTEP k values) for this wave's MI x NI blocks.
+  __device__ __forceinline__ static void read_frags(const char* la, const char* lb, int wm, int wn,
+                                                    int ks, u32x4_t* fa, u32x4_t* fb) {
 #pragma unroll
-    for (int ks = 0; ks < BK / KSTEP; ++ks) {
-      u32x4_t fa[MI], fb[NI];
+    for (int i = 0; i < MI; ++i) {
+      const int r0 = wm * WTM + i * 32;
+      if constexpr (A_KC) fa[i] = frag_kc(la, r0, ks);
+      else if constexpr (ESZ == 2) fa[i] = frag_mc_bf16<A_PITCH>(la, r0, ks);
+      else fa[i] = frag_mc_f32<A_PITCH>(la, r0, ks);
+    }
 #pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const int r0 = wm * WTM + i * 32;
-        if constexpr (A_KC) fa[i] = frag_kc(la, r0, ks);
-        else if constexpr (ESZ == 2) fa[i] = frag_mc_bf16<A_PITCH>(la, r0, ks);
-        else fa[i] = frag_mc_f32<A_PITCH>(la, r0, ks);
-      }
+    for (int j = 0; j < NI; ++j) {
+      const int r0 = wn * WTN + j * 32;
+      if constexpr (B_KC) fb[j] = frag_kc(lb, r0, ks);
+      else if constexpr (ESZ == 2) fb[j] = frag_mc_bf16<B_PITCH>(lb, r0, ks);
+      else fb[j] = frag_mc_f32<B_PITCH>(lb, r0, ks);
+    }
+  }
+
+  __device__ __forceinline__ void mma_all(const u32x4_t* fa, const u32x4_t* fb) {
 #pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        const int r0 = wn * WTN + j * 32;
-        if constexpr (B_KC) fb[j] = frag_kc(lb, r0, ks);
-        else if constexpr (ESZ == 2) fb[j] = frag_mc_bf16<B_PITCH>(lb, r0, ks);
-        else fb[j] = frag_mc_f32<B_PITCH>(lb, r0, ks);
-      }
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NI; ++j) mma(acc[i][j], fa[i], fb[j]);
+      for (int j = 0; j < NI; ++j) mma(acc[i][j], fa[i], fb[j]);
+  }
+
+  // Waits until at most n of this wave's vector-memory operations (here: the
+  // LDS DMA loads) are outstanding.  n is wave-uniform and small.
+  __device__ __forceinline__ static void wait_vm(int n) {
+    switch (n) {
+      // gfx9 encoding: vmcnt in bits 3:0, expcnt 6:4 and lgkmcnt 11:8 left at max
+      case 0: __builtin_amdgcn_s_waitcnt(0x0f70); break;
+      case 1: __builtin_amdgcn_s_waitcnt(0x0f71); break;
+      case 2: __builtin_amdgcn_s_waitcnt(0x0f72); break;
+      case 3: __builtin_amdgcn_s_waitcnt(0x0f73); break;
+      case 4: __builtin_amdgcn_s_waitcnt(0x0f74); break;
+      case 5: __builtin_amdgcn_s_waitcnt(0x0f75); break;
+      case 6: __builtin_amdgcn_s_waitcnt(0x0f76); break;
+      case 7: __builtin_amdgcn_s_waitcnt(0x0f77); break;
+      case 8: __builtin_amdgcn_s_waitcnt(0x0f78); break;
+      default: __builtin_amdgcn_s_waitcnt(0x0f70); break;
     }
   }
 
   // Full K loop for one tile: acc += A * B.  `lds` holds LDS_BYTES.  Ends with a
   // barrier, so the caller may reuse LDS (or start another tile) right away.
+  //
+  // LDS ring of NS stages filled by DMA, NS - 1 stages ahead of the MFMA work:
+  //   iteration kt: wait until stages kt and kt+1 have landed (this wave's
+  //   DMA count), barrier (they are then visible to every wave, and every
+  //   wave is done with stage kt-1), issue the DMA of stage kt+NS-1 into the
+  //   slot of kt-1, then run KS fragment steps on stage kt with fragments
+  //   double-buffered in registers; the last step already reads the first
+  //   fragments of stage kt+1.
   __device__ __forceinline__ void mainloop(const Operand& A, const Operand& B, int K, char* lds) {
+    if constexpr (DMA) mainloop_dma(A, B, K, lds);
+    else mainloop_regs(A, B, K, lds);
+  }
+
+  // Register-staged double buffer (NS == 2):
+  //   - fragments of step s+1 are read from LDS while step s's MFMAs run;
+  //   - the next stage, already in registers, is written to the other LDS
+  //     buffer after the second step and the loads of the stage after it are
+  //     issued right then (global latency hides behind ~1.5 stages);
+  //   - one barrier per stage.
+  __device__ __forceinline__ void mainloop_regs(const Operand& A, const Operand& B, int K, char* lds) {
+    static_assert(KS % 2 == 0 && KS >= 2, "fragment double buffer needs an even step count");
     const int wave = threadIdx.x >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const __amdgpu_buffer_rsrc_t rsa = make_rsrc(A.base, A.bytes);
     const __amdgpu_buffer_rsrc_t rsb = make_rsrc(B.base, B.bytes);
     const int nk = (K + BK - 1) / BK;
     if (nk <= 0) return;
+    u32x4_t ra[A_LD], rb[B_LD];
     gload<A_KC, BM, A_LD>(A, rsa, 0, ra);
     gload<B_KC, BN, B_LD>(B, rsb, 0, rb);
     lstore<A_KC, BM, A_PITCH, A_LD>(lds, ra);
     lstore<B_KC, BN, B_PITCH, B_LD>(lds + A_BYTES, rb);
+    if (nk > 1) {
+      gload<A_KC, BM, A_LD>(A, rsa, BK, ra);
+      gload<B_KC, BN, B_LD>(B, rsb, BK, rb);
+    }
     __syncthreads();
+    u32x4_t fa[2][MI], fb[2][NI];
+    read_frags(lds, lds + A_BYTES, wm, wn, 0, fa[0], fb[0]);
     for (int kt = 0; kt < nk; ++kt) {
-      char* cur = lds + (kt & 1) * STAGE;
+      const char* cur = lds + (kt & 1) * STAGE;
       char* nxt = lds + ((kt + 1) & 1) * STAGE;
-      const bool more = kt + 1 < nk;
-      if (more) {
-        gload<A_KC, BM, A_LD>(A, rsa, (kt + 1) * BK, ra);
-        gload<B_KC, BN, B_LD>(B, rsb, (kt + 1) * BK, rb);
-      }
-      compute_stage(cur, cur + A_BYTES, wm, wn);
-      if (more) {
-        lstore<A_KC, BM, A_PITCH, A_LD>(nxt, ra);
-        lstore<B_KC, BN, B_PITCH, B_LD>(nxt + A_BYTES, rb);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS)
+          read_frags(cur, cur + A_BYTES, wm, wn, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+        mma_all(fa[ks & 1], fb[ks & 1]);
+        if (ks == 1 && kt + 1 < nk) {
+          lstore<A_KC, BM, A_PITCH, A_LD>(nxt, ra);
+          lstore<B_KC, BN, B_PITCH, B_LD>(nxt + A_BYTES, rb);
+          if (kt + 2 < nk) {
+            gload<A_KC, BM, A_LD>(A, rsa, (kt + 2) * BK, ra);
+            gload<B_KC, BN, B_LD>(B, rsb, (kt + 2) * BK, rb);
+          }
+        }
       }
       __syncthreads();
+      if (kt + 1 < nk) read_frags(nxt, nxt + A_BYTES, wm, wn, 0, fa[0], fb[0]);
     }
+  }
+
+  __device__ __forceinline__ void mainloop_dma(const Operand& A, const Operand& B, int K, char* lds) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(A.base, A.bytes);
+    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(B.base, B.bytes);
+    const int nk = (K + BK - 1) / BK;
+    if (nk <= 0) return;
+    uint32_t offa[A_J], offb[B_J];
+    int ka[A_J], kb[B_J];
+    bool oka[A_J], okb[B_J];
+    dma_setup<A_KC, BM, A_PITCH, A_NB, A_J>(A, wave, offa, ka, oka);
+    dma_setup<B_KC, BN, B_PITCH, B_NB, B_J>(B, wave, offb, kb, okb);
+    // this wave's DMA instructions per stage
+    const int per_stage = min(A_J, (A_NB - wave + NW - 1) / NW) + min(B_J, (B_NB - wave + NW - 1) / NW);
+
+    auto issue = [&](int t) {
+      char* st = lds + (t % NS) * STAGE;
+      dma_issue<A_KC, A_NB, A_J>(A, rsa, wave, t * BK, st, offa, ka, oka);
+      dma_issue<B_KC, B_NB, B_J>(B, rsb, wave, t * BK, st + A_BYTES, offb, kb, okb);
+    };
+#pragma unroll
+    for (int t = 0; t < NS - 1; ++t)
+      if (t < nk) issue(t);
+
+    u32x4_t fa[2][MI], fb[2][NI];
+    for (int kt = 0; kt < nk; ++kt) {
+      // stages issued so far: 0 .. min(nk, kt + NS - 1) - 1; kt and kt + 1 must be done
+      const int issued = min(nk, kt + NS - 1);
+      const int later = max(0, issued - (kt + 2));
+      wait_vm(later * per_stage);
+      // A plain s_barrier: __syncthreads() would also drain every outstanding
+      // DMA (vmcnt(0)) and serialise the ring.  The "memory" clobber keeps the
+      // compiler from moving LDS accesses across it; this wave's reads of the
+      // stage being recycled have all been consumed by MFMAs already.
+      asm volatile("s_barrier" ::: "memory");
+      if (kt + NS - 1 < nk) issue(kt + NS - 1);
+      const char* cur = lds + (kt % NS) * STAGE;
+      if (kt == 0) read_frags(cur, cur + A_BYTES, wm, wn, 0, fa[0], fb[0]);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int nb = (ks + 1) & 1;
+        if (ks + 1 < KS) {
+          read_frags(cur, cur + A_BYTES, wm, wn, ks + 1, fa[nb], fb[nb]);
+        } else {
+          // first fragments of the next stage (unconditional, so that the
+          // LDS counter waits stay exact; after the last stage the read is
+          // of a stale slot and unused)
+          const char* nx = lds + ((kt + 1) % NS) * STAGE;
+          read_frags(nx, nx + A_BYTES, wm, wn, 0, fa[nb], fb[nb]);
+        }
+        mma_all(fa[ks & 1], fb[ks & 1]);
+      }
+      if constexpr (KS % 2 == 1) {
+        // the next stage's first fragments sit in set 1: move them to set 0
+#pragma unroll
+        for (int i = 0; i < MI; ++i) fa[0][i] = fa[1][i];
+#pragma unroll
+        for (int j = 0; j < NI; ++j) fb[0][j] = fb[1][j];
+      }
+    }
+    __syncthreads();
   }
 
   // Row (within the workgroup tile) of accumulator register r of block (i, *).
