@@ -71,15 +71,63 @@ def cpu_baseline(inp, cfg, n_rows: int):
             "seconds": dt, "host_cpus": os.cpu_count()}
 
 
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed profiler summary,
+    or None when there is none for this workload or the kernel sources have
+    changed since the counters were taken."""
+    import glob
+    import hashlib
+    for path in glob.glob(os.path.join(ROOT, "profiles", "traffic_*.json")):
+        try:
+            rec = json.load(open(path))
+        except (OSError, ValueError):
+            continue
+        if not rec.get("workload", "").startswith(workload):
+            continue
+        h = hashlib.sha256()
+        for f in rec.get("source_files", []):
+            try:
+                h.update(open(os.path.join(ROOT, f), "rb").read())
+            except OSError:
+                return None
+        if h.hexdigest() != rec.get("source_sha256"):
+            return None
+        k = rec.get("per_launch", {}).get(kernel)
+        return None if k is None else int(k["traffic_bytes"])
+    return None
+
+
+def copy_calibration(mib: int):
+    """A plain copy of mib MiB (read mib, write mib), three times: the byte
+    counters of a profiler run over it give the scale of FETCH_SIZE and
+    WRITE_SIZE against known traffic."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.randn(n, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copied {mib} MiB x 3")
+    print(json.dumps({"copy_calibration_bytes": n * 4, "copies": 3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3, help="workload index (default 3)")
-    ap.add_argument("--cpu-rows", type=int, default=2048,
+    ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of the CPU-oracle sample (0 skips it)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
+                    help="only run a plain device copy of this many MiB (a known-size "
+                         "reference for the HBM byte counters) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -165,7 +213,7 @@ def main():
     achieved = flops_per_launch / (avg_ms / 1e3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom_name, "achieved": round(achieved, 2),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": None, "flops_per_launch": flops_per_launch,
+                "traffic": measured_traffic(dom_name, cfg.name), "flops_per_launch": flops_per_launch,
                 "avg_launch_ms": round(avg_ms, 4), "launches": dom["launches"]}
 
     cpu = None

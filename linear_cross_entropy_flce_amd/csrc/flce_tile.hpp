@@ -90,6 +90,7 @@ struct Tile {
   static constexpr int KB = KB_;                 // bytes of k per KC row per stage
   static constexpr int NS = NS_;                 // LDS ring stages (2 without DMA)
   static constexpr bool DMA = DMA_;              // global -> LDS by DMA, else through VGPRs
+  static constexpr bool kAKC = A_KC, kBKC = B_KC;  // operand layouts
   static constexpr int BK = KB / ESZ;            // k per stage
   static constexpr int KSTEP = 2 * CW;           // k per fragment step
   static constexpr int KS = BK / KSTEP;          // fragment steps per stage
