@@ -31,8 +31,8 @@
  *     thread-local error string.  All work is ordered on `stream` (a
  *     hipStream_t; NULL means the default stream).
  *   - Requirements: T >= 0, V >= 1, d >= 8 and d % 8 == 0, T, V < 2^31,
- *     d <= 65536, device pointers 16-byte aligned.  Violations are reported
- *     before anything is launched.
+ *     d <= 65536, H and W each below 2 GiB, device pointers 16-byte aligned.
+ *     Violations are reported before anything is launched.
  *   - Results are bitwise reproducible for identical inputs and plan: every
  *     reduction runs in a fixed order, and no floating-point atomics are used.
  *   - Errors are returned as flce_status_t; nothing throws across the ABI.

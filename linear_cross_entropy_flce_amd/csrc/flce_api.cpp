@@ -218,6 +218,10 @@ flce_status_t flce_plan(int64_t T, int64_t d, int64_t V, flce_dtype_t dtype, uin
 
   const bool bf16 = dtype == FLCE_BF16;
   const int64_t esz = bf16 ? 2 : 4;
+  // the kernels address H and W through buffer resources with 32-bit offsets
+  if (T * d * esz >= (1ll << 31) || V * d * esz >= (1ll << 31))
+    return fail(FLCE_ERR_UNSUPPORTED, "H (%lld bytes) and W (%lld bytes) must each be below 2 GiB",
+                (long long)(T * d * esz), (long long)(V * d * esz));
   const flce::TileInfo ti = flce::tile_info(bf16);
   if (cap == 0) cap = kDefaultCap;
   // tile offsets into the workspace are 32-bit: keep it below 2 GiB

@@ -146,12 +146,14 @@ __global__ void __launch_bounds__(LogitCfg<E>::T::NT, 1)
   const int64_t t0 = (int64_t)tt * TL::BN;
 
   // B operand: H rows of this token tile (K-contiguous).
+  const __amdgpu_buffer_rsrc_t rsH = make_rsrc(a.H, clamp_bytes(a.T * a.d * ESZ));
+  const __amdgpu_buffer_rsrc_t rsW = make_rsrc(a.W, clamp_bytes((int64_t)a.V * a.d * ESZ));
   Operand B;
-  B.base = reinterpret_cast<const char*>(a.H) + t0 * a.d * ESZ;
+  B.rs = rsH;
+  B.off = (uint32_t)(t0 * a.d * ESZ);
   B.ld_bytes = (uint32_t)(a.d * ESZ);
   B.rows = (int)min<int64_t>(TL::BN, a.T - t0);
   B.cols = a.d;
-  B.bytes = clamp_bytes((a.T - t0) * a.d * ESZ);
 
   // Per-lane state for its NI token columns: running max and sum over the
   // vocab rows this lane holds, and the target (row index) of each column.
@@ -166,15 +168,14 @@ __global__ void __launch_bounds__(LogitCfg<E>::T::NT, 1)
   }
 
   TL tile;
+  Operand A;
+  A.rs = rsW;
+  A.ld_bytes = (uint32_t)(a.d * ESZ);
+  A.cols = a.d;
   for (int vt = vt_begin; vt < vt_end; ++vt) {
     const int64_t v0 = (int64_t)vt * TL::BM;
-    Operand A;
-    A.base = reinterpret_cast<const char*>(a.W) + v0 * a.d * ESZ;
-    A.ld_bytes = (uint32_t)(a.d * ESZ);
+    A.off = (uint32_t)(v0 * a.d * ESZ);
     A.rows = (int)min<int64_t>(TL::BM, a.V - v0);
-    A.cols = a.d;
-    A.bytes = clamp_bytes((a.V - v0) * a.d * ESZ);
-
     tile.zero();
     tile.mainloop(A, B, a.d, lds);
 
@@ -336,19 +337,18 @@ __global__ void __launch_bounds__(LogitCfg<E>::T::NT, 1) bwd_dz_kernel(DzArgs a)
   const int wm = wave / TL::WN, wn = wave % TL::WN;
   const int64_t v0 = a.v_begin + (int64_t)tm * TL::BM;  // global vocab id of tile row 0
   const int64_t tl0 = (int64_t)tn * TL::BN;             // token within the block
-  const int64_t t0 = a.t_begin + tl0;                   // global token
 
   Operand A, B;
-  A.base = reinterpret_cast<const char*>(a.W) + v0 * a.d * ESZ;
+  A.rs = make_rsrc(a.W, clamp_bytes((int64_t)a.V * a.d * ESZ));
+  A.off = (uint32_t)(v0 * a.d * ESZ);
   A.ld_bytes = (uint32_t)(a.d * ESZ);
   A.rows = (int)max<int64_t>(0, min<int64_t>(TL::BM, a.V - v0));
   A.cols = a.d;
-  A.bytes = clamp_bytes((a.V - v0) * a.d * ESZ);
-  B.base = reinterpret_cast<const char*>(a.H) + t0 * a.d * ESZ;
+  B.rs = make_rsrc(a.H, clamp_bytes(a.T * a.d * ESZ));
+  B.off = (uint32_t)((a.t_begin + tl0) * a.d * ESZ);
   B.ld_bytes = (uint32_t)(a.d * ESZ);
   B.rows = (int)min<int64_t>(TL::BN, a.t_count - tl0);
   B.cols = a.d;
-  B.bytes = clamp_bytes((a.T - t0) * a.d * ESZ);
 
   TL tile;
   tile.zero();
@@ -425,6 +425,8 @@ __global__ void __launch_bounds__(LogitCfg<E>::T::NT, 1) bwd_dz_kernel(DzArgs a)
 // dH[block] (+)= dZ[block, slab] * W[slab].  M = tokens, N = hidden, K = slab.
 // mode: 0 = first slab of several (write fp32 acc), 1 = middle (acc += ),
 // 2 = last of several (acc + partial -> dH in E), 3 = only slab (-> dH in E).
+// (The K loop over a whole slab is long, so the epilogue's read of the
+// partial costs little here; dW, with a short K loop, preloads instead.)
 template <typename E>
 __global__ void __launch_bounds__(DhCfg<E>::T::NT, 1) bwd_dh_kernel(DhArgs a) {
   using TL = typename DhCfg<E>::T;
@@ -438,16 +440,16 @@ __global__ void __launch_bounds__(DhCfg<E>::T::NT, 1) bwd_dh_kernel(DhArgs a) {
   const int64_t n0 = (int64_t)tn * TL::BN;   // hidden index
 
   Operand A, B;
-  A.base = reinterpret_cast<const char*>(a.dz) + tl0 * a.ldz * ESZ;
+  A.rs = make_rsrc(a.dz, clamp_bytes((int64_t)a.t_count * a.ldz * ESZ));
+  A.off = (uint32_t)(tl0 * a.ldz * ESZ);
   A.ld_bytes = (uint32_t)(a.ldz * ESZ);
   A.rows = (int)min<int64_t>(TL::BM, a.t_count - tl0);
   A.cols = a.k_count;
-  A.bytes = clamp_bytes((a.t_count - tl0) * a.ldz * ESZ);
-  B.base = reinterpret_cast<const char*>(a.W) + (a.v_begin * a.d + n0) * ESZ;
+  B.rs = make_rsrc(a.W, clamp_bytes((int64_t)a.V * a.d * ESZ));
+  B.off = (uint32_t)((a.v_begin * a.d + n0) * ESZ);
   B.ld_bytes = (uint32_t)(a.d * ESZ);
   B.rows = a.k_count;
   B.cols = (int)min<int64_t>(TL::BN, a.d - n0);
-  B.bytes = clamp_bytes(((int64_t)(a.V - a.v_begin) * a.d - n0) * ESZ);
 
   TL tile;
   tile.zero();
@@ -478,7 +480,8 @@ __global__ void __launch_bounds__(DhCfg<E>::T::NT, 1) bwd_dh_kernel(DhArgs a) {
 
 // ================================================================ backward dW
 // dW[slab] (+)= dZ[block, slab]^T * H[block].  M = slab vocab, N = hidden,
-// K = block tokens.  accumulate: 0 = overwrite, 1 = add to dW.
+// K = block tokens.  accumulate: 0 = overwrite, 1 = add to dW (the MFMA
+// accumulators start from the stored dW tile, so the epilogue only stores).
 template <typename E>
 __global__ void __launch_bounds__(DwCfg<E>::T::NT, 1) bwd_dw_kernel(DwArgs a) {
   using TL = typename DwCfg<E>::T;
@@ -492,19 +495,24 @@ __global__ void __launch_bounds__(DwCfg<E>::T::NT, 1) bwd_dw_kernel(DwArgs a) {
   const int64_t n0 = (int64_t)tn * TL::BN;
 
   Operand A, B;
-  A.base = reinterpret_cast<const char*>(a.dz) + vl0 * ESZ;
+  A.rs = make_rsrc(a.dz, clamp_bytes((int64_t)a.t_count * a.ldz * ESZ));
+  A.off = (uint32_t)(vl0 * ESZ);
   A.ld_bytes = (uint32_t)(a.ldz * ESZ);
   A.rows = a.t_count;
   A.cols = (int)min<int64_t>(TL::BM, a.ldz - vl0);
-  A.bytes = clamp_bytes((int64_t)a.t_count * a.ldz * ESZ - vl0 * ESZ);
-  B.base = reinterpret_cast<const char*>(a.H) + (a.t_begin * a.d + n0) * ESZ;
+  B.rs = make_rsrc(a.H, clamp_bytes(a.T * a.d * ESZ));
+  B.off = (uint32_t)((a.t_begin * a.d + n0) * ESZ);
   B.ld_bytes = (uint32_t)(a.d * ESZ);
   B.rows = a.t_count;
   B.cols = (int)min<int64_t>(TL::BN, a.d - n0);
-  B.bytes = clamp_bytes(((a.T - a.t_begin) * a.d - n0) * ESZ);
 
   TL tile;
-  tile.zero();
+  // token blocks after the first (or a caller's running sum) continue from dW
+  if (a.accumulate)
+    tile.load_acc(a.dW + (a.v_begin + vl0) * a.d + n0, a.d,
+                  (int)min<int64_t>(TL::BM, a.v_count - vl0), (int)min<int64_t>(TL::BN, a.d - n0));
+  else
+    tile.zero();
   tile.mainloop(A, B, a.t_count, lds);
 
 #pragma unroll
@@ -517,10 +525,7 @@ __global__ void __launch_bounds__(DwCfg<E>::T::NT, 1) bwd_dw_kernel(DwArgs a) {
       for (int r = 0; r < 16; ++r) {
         const int64_t vl = vl0 + TL::row_of(wm, i, r);
         if (vl >= a.v_count) continue;
-        float* p = a.dW + (a.v_begin + vl) * a.d + n;
-        float v = tile.acc[i][j][r];
-        if (a.accumulate) v += *p;
-        *p = v;
+        a.dW[(a.v_begin + vl) * a.d + n] = tile.acc[i][j][r];
       }
   }
 }

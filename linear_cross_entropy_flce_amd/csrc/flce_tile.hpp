@@ -59,13 +59,16 @@ __device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t rsrc, ui
   return __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
 }
 
-// A runtime description of one operand of one workgroup tile.
+// A runtime description of one operand of one workgroup tile.  `rs` covers the
+// whole matrix (every matrix the library reads is below 2 GiB, so 32-bit byte
+// offsets reach all of it and kOOB stays beyond every resource), and `off` is
+// the byte offset of the tile origin inside it.
 struct Operand {
-  const char* base;   // KC: row 0 of the tile, k = 0.  MC: k = 0, first tile column.
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t off;       // KC: row 0 of the tile, k = 0.  MC: k = 0, first tile column.
   uint32_t ld_bytes;  // distance between consecutive rows in memory, in bytes
-  uint32_t bytes;     // bytes readable from base (guards every load)
-  int rows;           // KC: valid tile rows (M or N) from base.  MC: valid k rows (K).
-  int cols;           // KC: K in elements.                        MC: valid tile columns.
+  int rows;           // KC: valid tile rows (M or N).  MC: valid k rows (K).
+  int cols;           // KC: K in elements.             MC: valid tile columns.
 };
 
 template <typename E>
@@ -119,6 +122,33 @@ struct Tile {
 
   f32x16_t acc[MI][NI];
 
+  // acc = C[tile] for a row-major fp32 matrix (row pitch ldc elements) whose
+  // tile origin is `c`; `rows` x `cols` of it are valid.  The buffer resource
+  // ends at the last valid element, so rows past `rows` read as 0; columns
+  // past `cols` may read neighbouring elements of valid rows, which only
+  // reach accumulators that are never stored.  Loads are issued before the K
+  // loop, whose prologue hides their latency.
+  __device__ __forceinline__ void load_acc(const float* c, int64_t ldc, int rows, int cols) {
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int64_t bytes = rows > 0 && cols > 0 ? ((int64_t)(rows - 1) * ldc + cols) * 4 : 0;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(c, (uint32_t)(bytes > 0x7fffffff ? 0x7fffffff : bytes));
+    const uint32_t ld4 = (uint32_t)ldc * 4u;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j) {
+        const uint32_t base = (uint32_t)row_of(wm, i, 0) * ld4 + (uint32_t)col_of(wn, j) * 4u;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t soff = (uint32_t)(8 * (r >> 2) + (r & 3)) * ld4;
+          acc[i][j][r] = __builtin_bit_cast(
+              float, __builtin_amdgcn_raw_buffer_load_b32(rs, base, __builtin_amdgcn_readfirstlane(soff), 0));
+        }
+      }
+  }
+
   __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int i = 0; i < MI; ++i)
@@ -154,13 +184,13 @@ struct Tile {
       if constexpr (KC) {
         const int row = b * RPB + lane / CPR;
         const int kc = (lane % CPR) ^ swz(row);
-        off[j] = (uint32_t)row * op.ld_bytes + (uint32_t)kc * 16;
+        off[j] = op.off + (uint32_t)row * op.ld_bytes + (uint32_t)kc * 16;
         krel[j] = kc * CW;
         ok[j] = b < NB && row < op.rows;
       } else {
         const int o = b * 1024 + 16 * lane;
         const int kr = o / PITCH, cb = o % PITCH;
-        off[j] = (uint32_t)kr * op.ld_bytes + (uint32_t)cb;
+        off[j] = op.off + (uint32_t)kr * op.ld_bytes + (uint32_t)cb;
         krel[j] = kr;
         ok[j] = b < NB && kr < BK && cb < ROWS * ESZ && (cb / 16) * CW < op.cols;
       }
@@ -168,8 +198,7 @@ struct Tile {
   }
 
   template <bool KC, int NB, int J>
-  __device__ __forceinline__ static void dma_issue(const Operand& op, __amdgpu_buffer_rsrc_t rs,
-                                                   int wave, int k0, char* dst,
+  __device__ __forceinline__ static void dma_issue(const Operand& op, int wave, int k0, char* dst,
                                                    const uint32_t* off, const int* krel,
                                                    const bool* ok) {
 #pragma unroll
@@ -186,8 +215,8 @@ struct Tile {
           o = off[j] + (uint32_t)k0 * op.ld_bytes;
         }
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (__attribute__((address_space(3))) void*)(dst + b * 1024), 16, v ? o : kOOB, 0, 0,
-            0);
+            op.rs, (__attribute__((address_space(3))) void*)(dst + b * 1024), 16, v ? o : kOOB, 0,
+            0, 0);
       }
     }
   }
@@ -196,8 +225,7 @@ struct Tile {
   // Thread c of the workgroup moves chunk c, c + NT, ... of the stage: KC rows
   // are CPR chunks wide, MC rows ROWS * ESZ / 16 chunks.
   template <bool KC, int ROWS, int NLD>
-  __device__ __forceinline__ static void gload(const Operand& op, __amdgpu_buffer_rsrc_t rs,
-                                               int k0, u32x4_t* r) {
+  __device__ __forceinline__ static void gload(const Operand& op, int k0, u32x4_t* r) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
@@ -206,16 +234,18 @@ struct Tile {
       if constexpr (KC) {
         const int row = c / CPR, kc = c % CPR;
         const int k = k0 + kc * CW;
-        off = (row < op.rows && k < op.cols) ? (uint32_t)row * op.ld_bytes + (uint32_t)k * ESZ
-                                             : kOOB;
+        off = (row < op.rows && k < op.cols)
+                  ? op.off + (uint32_t)row * op.ld_bytes + (uint32_t)k * ESZ
+                  : kOOB;
       } else {
         constexpr int RC = ROWS * ESZ / 16;
         const int kr = c / RC, cc = c % RC;
         const int k = k0 + kr;
-        off = (k < op.rows && cc * CW < op.cols) ? (uint32_t)k * op.ld_bytes + (uint32_t)cc * 16
-                                                 : kOOB;
+        off = (k < op.rows && cc * CW < op.cols)
+                  ? op.off + (uint32_t)k * op.ld_bytes + (uint32_t)cc * 16
+                  : kOOB;
       }
-      r[i] = buffer_load16(rs, off);
+      r[i] = buffer_load16(op.rs, off);
     }
   }
 
@@ -358,18 +388,16 @@ struct Tile {
     static_assert(KS % 2 == 0 && KS >= 2, "fragment double buffer needs an even step count");
     const int wave = threadIdx.x >> 6;
     const int wm = wave / WN, wn = wave % WN;
-    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(A.base, A.bytes);
-    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(B.base, B.bytes);
     const int nk = (K + BK - 1) / BK;
     if (nk <= 0) return;
     u32x4_t ra[A_LD], rb[B_LD];
-    gload<A_KC, BM, A_LD>(A, rsa, 0, ra);
-    gload<B_KC, BN, B_LD>(B, rsb, 0, rb);
+    gload<A_KC, BM, A_LD>(A, 0, ra);
+    gload<B_KC, BN, B_LD>(B, 0, rb);
     lstore<A_KC, BM, A_PITCH, A_LD>(lds, ra);
     lstore<B_KC, BN, B_PITCH, B_LD>(lds + A_BYTES, rb);
     if (nk > 1) {
-      gload<A_KC, BM, A_LD>(A, rsa, BK, ra);
-      gload<B_KC, BN, B_LD>(B, rsb, BK, rb);
+      gload<A_KC, BM, A_LD>(A, BK, ra);
+      gload<B_KC, BN, B_LD>(B, BK, rb);
     }
     __syncthreads();
     u32x4_t fa[2][MI], fb[2][NI];
@@ -386,8 +414,8 @@ struct Tile {
           lstore<A_KC, BM, A_PITCH, A_LD>(nxt, ra);
           lstore<B_KC, BN, B_PITCH, B_LD>(nxt + A_BYTES, rb);
           if (kt + 2 < nk) {
-            gload<A_KC, BM, A_LD>(A, rsa, (kt + 2) * BK, ra);
-            gload<B_KC, BN, B_LD>(B, rsb, (kt + 2) * BK, rb);
+            gload<A_KC, BM, A_LD>(A, (kt + 2) * BK, ra);
+            gload<B_KC, BN, B_LD>(B, (kt + 2) * BK, rb);
           }
         }
       }
@@ -399,8 +427,6 @@ struct Tile {
   __device__ __forceinline__ void mainloop_dma(const Operand& A, const Operand& B, int K, char* lds) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / WN, wn = wave % WN;
-    const __amdgpu_buffer_rsrc_t rsa = make_rsrc(A.base, A.bytes);
-    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(B.base, B.bytes);
     const int nk = (K + BK - 1) / BK;
     if (nk <= 0) return;
     uint32_t offa[A_J], offb[B_J];
@@ -413,8 +439,8 @@ struct Tile {
 
     auto issue = [&](int t) {
       char* st = lds + (t % NS) * STAGE;
-      dma_issue<A_KC, A_NB, A_J>(A, rsa, wave, t * BK, st, offa, ka, oka);
-      dma_issue<B_KC, B_NB, B_J>(B, rsb, wave, t * BK, st + A_BYTES, offb, kb, okb);
+      dma_issue<A_KC, A_NB, A_J>(A, wave, t * BK, st, offa, ka, oka);
+      dma_issue<B_KC, B_NB, B_J>(B, wave, t * BK, st + A_BYTES, offb, kb, okb);
     };
 #pragma unroll
     for (int t = 0; t < NS - 1; ++t)

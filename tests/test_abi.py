@@ -64,6 +64,8 @@ def test_version_and_status_strings(lib):
     ((10, 12, 1000, 1), flce.FLCE_ERR_UNSUPPORTED),
     ((10, 65544, 1000, 1), flce.FLCE_ERR_UNSUPPORTED),
     ((1 << 31, 128, 1000, 1), flce.FLCE_ERR_UNSUPPORTED),
+    ((1 << 20, 1024, 1000, 1), flce.FLCE_ERR_UNSUPPORTED),   # H of 2 GiB
+    ((1000, 4096, 1 << 18, 0), flce.FLCE_ERR_UNSUPPORTED),   # fp32 W of 4 GiB
 ])
 def test_plan_rejects(lib, args, status):
     st, _ = flce.flce_plan_status(*args)
