@@ -62,8 +62,11 @@ __device__ __forceinline__ float dz_arg(float z, float lse, float log2g, float b
 #ifndef FLCE_DW_NS
 #define FLCE_DW_NS 2
 #endif
+#ifndef FLCE_BIG_WN
+#define FLCE_BIG_WN 4
+#endif
 template <typename E, bool A_KC, bool B_KC, int NS>
-using BigTile = Tile<256, 256, 2, 4, E, A_KC, B_KC, NS == 2 ? 128 : 64, NS, NS != 2>;
+using BigTile = Tile<256, 256, 2, FLCE_BIG_WN, E, A_KC, B_KC, NS == 2 ? 128 : 64, NS, NS != 2>;
 template <typename E, bool A_KC, bool B_KC, int NS>
 using SmallTile = Tile<128, 128, 2, 2, E, A_KC, B_KC, NS == 2 ? 128 : 64, NS, NS != 2>;
 

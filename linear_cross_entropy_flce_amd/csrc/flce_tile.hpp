@@ -249,6 +249,44 @@ struct Tile {
     }
   }
 
+  // Per-thread part of gload's offsets, fixed for the whole K loop: the
+  // tile-relative byte offset of each of this thread's chunks at k0 = 0, or
+  // kOOB when the chunk's row (KC) / column (MC) lies outside the operand.
+  // The stage's k then enters as the instruction's scalar offset, so a full
+  // stage costs no vector arithmetic; `kk` keeps each chunk's k (KC: element
+  // offset in the row, MC: row in the stage) for the partial last stage.
+  template <bool KC, int ROWS, int NLD>
+  __device__ __forceinline__ static void gprep(const Operand& op, uint32_t* voff, int* kk) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int c = tid + NT * i;
+      if constexpr (KC) {
+        const int row = c / CPR, kc = c % CPR;
+        voff[i] = row < op.rows ? op.off + (uint32_t)row * op.ld_bytes + (uint32_t)kc * 16 : kOOB;
+        kk[i] = kc * CW;
+      } else {
+        constexpr int RC = ROWS * ESZ / 16;
+        const int kr = c / RC, cc = c % RC;
+        voff[i] = cc * CW < op.cols ? op.off + (uint32_t)kr * op.ld_bytes + (uint32_t)cc * 16 : kOOB;
+        kk[i] = kr;
+      }
+    }
+  }
+
+  // Loads of the stage starting at k0.  `full`: the whole stage lies below K.
+  template <bool KC, int NLD>
+  __device__ __forceinline__ static void gload_fast(const Operand& op, const uint32_t* voff,
+                                                    const int* kk, int k0, bool full, u32x4_t* r) {
+    const int kmax = KC ? op.cols : op.rows;  // K
+    const uint32_t soff = KC ? (uint32_t)k0 * ESZ : (uint32_t)k0 * op.ld_bytes;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const uint32_t v = (full || k0 + kk[i] < kmax) ? voff[i] : kOOB;
+      r[i] = __builtin_amdgcn_raw_buffer_load_b128(op.rs, v, soff, 0);
+    }
+  }
+
   template <bool KC, int ROWS, int PITCH, int NLD>
   __device__ __forceinline__ static void lstore(char* lds, const u32x4_t* r) {
     const int tid = threadIdx.x;
@@ -378,49 +416,68 @@ struct Tile {
     else mainloop_regs(A, B, K, lds);
   }
 
-  // Register-staged double buffer (NS == 2):
+  // Register-staged double buffer (NS == 2), LDS laid out [A0 A1 B0 B1] so
+  // that with the stage parity fixed (loop unrolled by two) every LDS
+  // address is a per-thread base plus an immediate:
   //   - fragments of step s+1 are read from LDS while step s's MFMAs run;
   //   - the next stage, already in registers, is written to the other LDS
   //     buffer after the second step and the loads of the stage after it are
   //     issued right then (global latency hides behind ~1.5 stages);
   //   - one barrier per stage.
+  template <int P>
+  __device__ __forceinline__ void regs_stage(const Operand& A, const Operand& B, char* lds, int kt,
+                                             int nk, int K, int wm, int wn, const uint32_t* va,
+                                             const int* ka, const uint32_t* vb, const int* kb,
+                                             u32x4_t* ra, u32x4_t* rb, u32x4_t (*fa)[MI],
+                                             u32x4_t (*fb)[NI]) {
+    const char* ca = lds + P * A_BYTES;
+    const char* cb = lds + 2 * A_BYTES + P * B_BYTES;
+    char* na = lds + (1 - P) * A_BYTES;
+    char* nb = lds + 2 * A_BYTES + (1 - P) * B_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) read_frags(ca, cb, wm, wn, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+      mma_all(fa[ks & 1], fb[ks & 1]);
+      if (ks == 1 && kt + 1 < nk) {
+        lstore<A_KC, BM, A_PITCH, A_LD>(na, ra);
+        lstore<B_KC, BN, B_PITCH, B_LD>(nb, rb);
+        if (kt + 2 < nk) {
+          const int k0 = (kt + 2) * BK;
+          const bool full = k0 + BK <= K;
+          gload_fast<A_KC, A_LD>(A, va, ka, k0, full, ra);
+          gload_fast<B_KC, B_LD>(B, vb, kb, k0, full, rb);
+        }
+      }
+    }
+    __syncthreads();
+    if (kt + 1 < nk) read_frags(na, nb, wm, wn, 0, fa[0], fb[0]);
+  }
+
   __device__ __forceinline__ void mainloop_regs(const Operand& A, const Operand& B, int K, char* lds) {
     static_assert(KS % 2 == 0 && KS >= 2, "fragment double buffer needs an even step count");
     const int wave = threadIdx.x >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int nk = (K + BK - 1) / BK;
     if (nk <= 0) return;
+    uint32_t va[A_LD], vb[B_LD];
+    int ka[A_LD], kb[B_LD];
+    gprep<A_KC, BM, A_LD>(A, va, ka);
+    gprep<B_KC, BN, B_LD>(B, vb, kb);
     u32x4_t ra[A_LD], rb[B_LD];
-    gload<A_KC, BM, A_LD>(A, 0, ra);
-    gload<B_KC, BN, B_LD>(B, 0, rb);
+    gload_fast<A_KC, A_LD>(A, va, ka, 0, BK <= K, ra);
+    gload_fast<B_KC, B_LD>(B, vb, kb, 0, BK <= K, rb);
     lstore<A_KC, BM, A_PITCH, A_LD>(lds, ra);
-    lstore<B_KC, BN, B_PITCH, B_LD>(lds + A_BYTES, rb);
+    lstore<B_KC, BN, B_PITCH, B_LD>(lds + 2 * A_BYTES, rb);
     if (nk > 1) {
-      gload<A_KC, BM, A_LD>(A, BK, ra);
-      gload<B_KC, BN, B_LD>(B, BK, rb);
+      gload_fast<A_KC, A_LD>(A, va, ka, BK, 2 * BK <= K, ra);
+      gload_fast<B_KC, B_LD>(B, vb, kb, BK, 2 * BK <= K, rb);
     }
     __syncthreads();
     u32x4_t fa[2][MI], fb[2][NI];
-    read_frags(lds, lds + A_BYTES, wm, wn, 0, fa[0], fb[0]);
-    for (int kt = 0; kt < nk; ++kt) {
-      const char* cur = lds + (kt & 1) * STAGE;
-      char* nxt = lds + ((kt + 1) & 1) * STAGE;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ks + 1 < KS)
-          read_frags(cur, cur + A_BYTES, wm, wn, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
-        mma_all(fa[ks & 1], fb[ks & 1]);
-        if (ks == 1 && kt + 1 < nk) {
-          lstore<A_KC, BM, A_PITCH, A_LD>(nxt, ra);
-          lstore<B_KC, BN, B_PITCH, B_LD>(nxt + A_BYTES, rb);
-          if (kt + 2 < nk) {
-            gload<A_KC, BM, A_LD>(A, (kt + 2) * BK, ra);
-            gload<B_KC, BN, B_LD>(B, (kt + 2) * BK, rb);
-          }
-        }
-      }
-      __syncthreads();
-      if (kt + 1 < nk) read_frags(nxt, nxt + A_BYTES, wm, wn, 0, fa[0], fb[0]);
+    read_frags(lds, lds + 2 * A_BYTES, wm, wn, 0, fa[0], fb[0]);
+    for (int kt = 0; kt < nk; kt += 2) {
+      regs_stage<0>(A, B, lds, kt, nk, K, wm, wn, va, ka, vb, kb, ra, rb, fa, fb);
+      if (kt + 1 < nk) regs_stage<1>(A, B, lds, kt + 1, nk, K, wm, wn, va, ka, vb, kb, ra, rb, fa, fb);
     }
   }
 
