@@ -97,6 +97,96 @@ def measured_traffic(kernel: str, workload: str):
     return None
 
 
+TRAFFIC_SOURCES = ["linear_cross_entropy_flce_amd/csrc/flce_kernels.hip",
+                   "linear_cross_entropy_flce_amd/csrc/flce_tile.hpp"]
+
+
+def summarize_traffic(fetch_csv: str, write_csv: str, cfetch_csv: str, cwrite_csv: str,
+                      workload: str) -> dict:
+    """HBM bytes per launch of each library kernel from four rocprofv3
+    counter-collection CSVs: FETCH_SIZE and WRITE_SIZE over bench steps, and
+    the same two counters over --copy-calibration, whose copy kernel moves a
+    known number of bytes and so gives each counter's scale."""
+    import csv
+    import hashlib
+    import re
+    from collections import defaultdict
+
+    def per_dispatch(path, counter):
+        vals, names = defaultdict(float), {}
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                k = int(r["Dispatch_Id"])
+                vals[k] += float(r["Counter_Value"])
+                names[k] = r["Kernel_Name"]
+        return vals, names
+
+    def scale(path, counter):
+        vals, names = per_dispatch(path, counter)
+        copies = [v for k, v in vals.items() if "copyBuffer" in names[k]]
+        if not copies:
+            raise SystemExit(f"{path}: no copy kernel found")
+        return sum(copies) / len(copies) * 1024.0  # counter bytes per copy
+
+    def short(name):
+        m = re.search(r"flce(?:::|\d+)(\w+?)_kernel", name)
+        return m.group(1) if m else None
+
+    # each copy of bench.py --copy-calibration 1024 reads and writes 1 GiB
+    cal_bytes = 1024 * (1 << 20)
+    f_per_byte = scale(cfetch_csv, "FETCH_SIZE") / cal_bytes
+    w_per_byte = scale(cwrite_csv, "WRITE_SIZE") / cal_bytes
+    fv, fn = per_dispatch(fetch_csv, "FETCH_SIZE")
+    wv, wn = per_dispatch(write_csv, "WRITE_SIZE")
+    agg = defaultdict(lambda: {"n": 0, "fetch": 0.0, "nw": 0, "write": 0.0})
+    for k, v in fv.items():
+        n = short(fn[k])
+        if n:
+            agg[n]["n"] += 1
+            agg[n]["fetch"] += v
+    for k, v in wv.items():
+        n = short(wn[k])
+        if n:
+            agg[n]["nw"] += 1
+            agg[n]["write"] += v
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    per = {}
+    for n, a in agg.items():
+        if not a["n"] or not a["nw"]:
+            continue
+        fk, wk = a["fetch"] / a["n"], a["write"] / a["nw"]
+        rd, wr = fk * 1024 / f_per_byte, wk * 1024 / w_per_byte
+        per[n] = {"launches_profiled": a["n"], "fetch_kib_raw": round(fk, 1),
+                  "write_kib_raw": round(wk, 1), "read_bytes": int(rd), "write_bytes": int(wr),
+                  "traffic_bytes": int(rd + wr)}
+    return {
+        "about": "HBM traffic per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per "
+                 "dispatch), each divided by the value the same counter reads per byte of a plain "
+                 "1 GiB device copy (bench.py --copy-calibration 1024). Valid only while the "
+                 "kernel sources hash to source_sha256.",
+        "workload": workload,
+        "source_files": TRAFFIC_SOURCES,
+        "source_sha256": h.hexdigest(),
+        "calibration": {"copy_bytes": cal_bytes,
+                        "fetch_counter_bytes_per_byte": round(f_per_byte, 4),
+                        "write_counter_bytes_per_byte": round(w_per_byte, 4)},
+        "commands": [
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/fetch -o run -- python3 bench.py --steps 1 --warmup 0 --cpu-rows 0",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/write -o run -- python3 bench.py --steps 1 --warmup 0 --cpu-rows 0",
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/cfetch -o run -- python3 bench.py --copy-calibration 1024",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/cwrite -o run -- python3 bench.py --copy-calibration 1024",
+            "python3 bench.py --traffic-summary OUT/fetch/run_counter_collection.csv "
+            "OUT/write/run_counter_collection.csv OUT/cfetch/run_counter_collection.csv "
+            "OUT/cwrite/run_counter_collection.csv",
+        ],
+        "per_launch": per,
+    }
+
+
 def copy_calibration(mib: int):
     """A plain copy of mib MiB (read mib, write mib), three times: the byte
     counters of a profiler run over it give the scale of FETCH_SIZE and
@@ -119,14 +209,24 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3, help="workload index (default 3)")
-    ap.add_argument("--cpu-rows", type=int, default=4096,
+    ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="rows of the CPU-oracle sample (0 skips it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this many MiB (a known-size "
                          "reference for the HBM byte counters) and exit")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH", "WRITE", "CFETCH", "CWRITE"),
+                    help="only turn four rocprofv3 counter CSVs (FETCH_SIZE and WRITE_SIZE over "
+                         "bench steps, then over --copy-calibration 1024) into the per-launch "
+                         "traffic JSON that bench.py reads from profiles/, print it and exit")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.traffic_summary:
+        import workloads as wl
+        print(json.dumps(summarize_traffic(*args.traffic_summary,
+                                           workload=wl.CONFIGS[args.config].name + " (one bench step)"),
+                         indent=1))
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

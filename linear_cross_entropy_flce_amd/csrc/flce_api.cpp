@@ -125,7 +125,7 @@ class Timed {
 double backward_cost(int64_t T, int64_t d, int64_t V, int64_t B, int64_t Vs,
                      const flce::TileInfo& ti) {
   const double unit = 256.0 * 256.0 * 256.0;
-  const int64_t n_dt_h = cdiv(d, ti.dh_bn), n_dt_w = cdiv(d, ti.dw_bn);
+  const int64_t n_dt_h = cdiv(d, ti.dh_bn), n_dt_w = cdiv(d, ti.dw_bm);
   double cost = 0;
   for (int64_t t0 = 0; t0 < T; t0 += B) {
     const int64_t tc = T - t0 < B ? T - t0 : B;
@@ -133,7 +133,7 @@ double backward_cost(int64_t T, int64_t d, int64_t V, int64_t B, int64_t Vs,
       const int64_t vc = V - v0 < Vs ? V - v0 : Vs;
       const int64_t dz_tiles = cdiv(vc, ti.logit_bm) * cdiv(tc, ti.logit_bn);
       const int64_t dh_tiles = cdiv(tc, ti.dh_bm) * n_dt_h;
-      const int64_t dw_tiles = cdiv(vc, ti.dw_bm) * n_dt_w;
+      const int64_t dw_tiles = cdiv(vc, ti.dw_bn) * n_dt_w;
       const double dz_tile = (double)ti.logit_bm * ti.logit_bn * d / unit;
       const double dh_tile = (double)ti.dh_bm * ti.dh_bn * vc / unit;
       const double dw_tile = (double)ti.dw_bm * ti.dw_bn * tc / unit;
@@ -468,8 +468,8 @@ flce_status_t flce_backward(const flce_plan_t* plan, const void* H, const void* 
       w.t_count = t_count;
       w.v_begin = v_begin;
       w.v_count = v_count;
-      w.n_mtiles = (int)cdiv(v_count, ti.dw_bm);
-      w.n_ntiles = (int)cdiv(p.d, ti.dw_bn);
+      w.n_mtiles = (int)cdiv(p.d, ti.dw_bm);
+      w.n_ntiles = (int)cdiv(v_count, ti.dw_bn);
       w.accumulate = (b > 0 || accumulate_dW) ? 1 : 0;
       w.dW = dW;
       Timed t_dw(s, K_BWD_DW, 2.0 * tc * dd * vc,

@@ -19,6 +19,7 @@
 //   bwd_dh      dH_block (+)= dZ W_slab   (fp32 accumulate, cast at the end).
 //   bwd_dw      dW_slab (+)= dZ^T H_block (fp32, deterministic block order).
 #include <hip/hip_runtime.h>
+
 #include <math.h>
 #include <stdint.h>
 
@@ -65,8 +66,26 @@ __device__ __forceinline__ float dz_arg(float z, float lse, float log2g, float b
 #ifndef FLCE_BIG_WN
 #define FLCE_BIG_WN 4
 #endif
-template <typename E, bool A_KC, bool B_KC, int NS>
-using BigTile = Tile<256, 256, 2, FLCE_BIG_WN, E, A_KC, B_KC, NS == 2 ? 128 : 64, NS, NS != 2>;
+#ifndef FLCE_LOGIT_KB
+#define FLCE_LOGIT_KB 128
+#endif
+#ifndef FLCE_DH_KB
+#define FLCE_DH_KB 128
+#endif
+#ifndef FLCE_DW_KB
+#define FLCE_DW_KB 128
+#endif
+#ifndef FLCE_LOGIT_DMA
+#define FLCE_LOGIT_DMA 0
+#endif
+#ifndef FLCE_DH_DMA
+#define FLCE_DH_DMA 0
+#endif
+#ifndef FLCE_DW_DMA
+#define FLCE_DW_DMA 0
+#endif
+template <typename E, bool A_KC, bool B_KC, int NS, int KB, bool DMA>
+using BigTile = Tile<256, 256, 2, FLCE_BIG_WN, E, A_KC, B_KC, KB, NS, DMA || NS != 2>;
 template <typename E, bool A_KC, bool B_KC, int NS>
 using SmallTile = Tile<128, 128, 2, 2, E, A_KC, B_KC, NS == 2 ? 128 : 64, NS, NS != 2>;
 
@@ -75,20 +94,20 @@ template <typename E>
 struct LogitCfg;
 template <>
 struct LogitCfg<__bf16> {
-  using T = BigTile<__bf16, true, true, FLCE_LOGIT_NS>;
+  using T = BigTile<__bf16, true, true, FLCE_LOGIT_NS, FLCE_LOGIT_KB, FLCE_LOGIT_DMA>;
 };
 template <>
 struct LogitCfg<float> {
   using T = SmallTile<float, true, true, FLCE_LOGIT_NS>;
 };
 
-// dH (A = dZ K-contiguous, B = W MN-contiguous) and dW (A = dZ MN-contiguous,
-// B = H MN-contiguous).
+// dH (A = dZ K-contiguous, B = W MN-contiguous) and dW^T (A = H, B = dZ, both
+// MN-contiguous).
 template <typename E>
 struct DhCfg;
 template <>
 struct DhCfg<__bf16> {
-  using T = BigTile<__bf16, true, false, FLCE_DH_NS>;
+  using T = BigTile<__bf16, true, false, FLCE_DH_NS, FLCE_DH_KB, FLCE_DH_DMA>;
 };
 template <>
 struct DhCfg<float> {
@@ -98,7 +117,7 @@ template <typename E>
 struct DwCfg;
 template <>
 struct DwCfg<__bf16> {
-  using T = BigTile<__bf16, false, false, FLCE_DW_NS>;
+  using T = BigTile<__bf16, false, false, FLCE_DW_NS, FLCE_DW_KB, FLCE_DW_DMA>;
 };
 template <>
 struct DwCfg<float> {
@@ -325,17 +344,55 @@ __device__ __forceinline__ void store4<float>(float* p, float a, float b, float 
   *reinterpret_cast<f32x4_t*>(p) = f32x4_t{a, b, c, d};
 }
 
+// Writes a finished bf16 dZ tile (vocab x token in the accumulators) to the
+// token-major workspace through LDS, so that each store instruction covers
+// whole 512-byte token rows instead of 32 scattered 8-byte pieces.  LDS holds
+// the tile as [token][vocab] with its 8-byte granules XOR-swizzled by the
+// token (granule g of row c sits at g ^ (c % 32)), which keeps both the
+// 8-byte writes (32 tokens, one granule) and the 16-byte row reads free of
+// bank conflicts.  Needs BN * BM * 2 bytes of LDS; the caller's mainloop has
+// ended with a barrier.
+template <typename TL>
+__device__ __forceinline__ void store_dz_tile(const TL& tile, char* lds, __bf16* dz, int64_t ldz,
+                                              int64_t vl0, int64_t ldz_cols, int64_t tl0,
+                                              int64_t t_count, int wm, int wn) {
+  static_assert(TL::BM == 256 && TL::ESZ == 2, "token rows of 512 bytes");
+  static_assert(TL::BN * TL::BM * 2 <= TL::LDS_BYTES, "tile fits the mainloop's LDS");
+#pragma unroll
+  for (int j = 0; j < TL::NI; ++j) {
+    const int c = TL::col_of(wn, j);
+#pragma unroll
+    for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int g = TL::row_of(wm, i, rq * 4) >> 2;
+        bf16x4_t v = {(__bf16)tile.acc[i][j][rq * 4], (__bf16)tile.acc[i][j][rq * 4 + 1],
+                      (__bf16)tile.acc[i][j][rq * 4 + 2], (__bf16)tile.acc[i][j][rq * 4 + 3]};
+        *reinterpret_cast<bf16x4_t*>(lds + c * 512 + ((g ^ (c & 31)) << 3)) = v;
+      }
+  }
+  __syncthreads();
+  constexpr int kChunks = TL::BN * 32 / TL::NT;  // 16-byte chunks per thread
+#pragma unroll
+  for (int it = 0; it < kChunks; ++it) {
+    const int idx = it * TL::NT + (int)threadIdx.x;
+    const int c = idx >> 5, m = idx & 31, x = c & 31;
+    u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds + c * 512 + ((m ^ (x >> 1)) << 4));
+    if (x & 1) v = u32x4_t{v[2], v[3], v[0], v[1]};
+    const int64_t vl = vl0 + 8 * m;
+    if (tl0 + c < t_count && vl < ldz_cols)
+      *reinterpret_cast<u32x4_t*>(dz + (tl0 + c) * ldz + vl) = v;
+  }
+}
+
 // One 256 x 256 (vocab x token) tile of the block/slab: recompute logits,
 // form dZ, write it token-major: dz[t_local * ldz + v_local].  Vocab rows past
 // V inside the slab's last tile are written as zeros so the contractions can
 // read whole 16-byte chunks.
 template <typename E>
-__global__ void __launch_bounds__(LogitCfg<E>::T::NT, 1) bwd_dz_kernel(DzArgs a) {
+__device__ __forceinline__ void dz_tile(const DzArgs& a, int tm, int tn, char* lds) {
   using TL = typename LogitCfg<E>::T;
-  extern __shared__ __attribute__((aligned(16))) char lds[];
   constexpr int ESZ = TL::ESZ;
-  int tm, tn;
-  if (!xcd_tile(blockIdx.x, a.n_vtiles, a.n_ttiles, 4, tm, tn)) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int wm = wave / TL::WN, wn = wave % TL::WN;
   const int64_t v0 = a.v_begin + (int64_t)tm * TL::BM;  // global vocab id of tile row 0
@@ -410,18 +467,30 @@ __global__ void __launch_bounds__(LogitCfg<E>::T::NT, 1) bwd_dz_kernel(DzArgs a)
         for (int r = 0; r < 16; ++r)
           if (i * 32 + 8 * (r >> 2) + (r & 3) >= lim) tile.acc[i][j][r] = 0.f;
     }
-    if (!col_ok) continue;
+    if constexpr (ESZ == 4) {
+      if (!col_ok) continue;
 #pragma unroll
-    for (int i = 0; i < TL::MI; ++i)
+      for (int i = 0; i < TL::MI; ++i)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int row0 = TL::row_of(wm, i, rq * 4);
-        const int64_t vl = v0 - a.v_begin + row0;  // vocab within the slab
-        if (vl < a.ldz_cols)
-          store4<E>(dz + tl * a.ldz + vl, tile.acc[i][j][rq * 4], tile.acc[i][j][rq * 4 + 1],
-                    tile.acc[i][j][rq * 4 + 2], tile.acc[i][j][rq * 4 + 3]);
-      }
+        for (int rq = 0; rq < 4; ++rq) {
+          const int row0 = TL::row_of(wm, i, rq * 4);
+          const int64_t vl = v0 - a.v_begin + row0;  // vocab within the slab
+          if (vl < a.ldz_cols)
+            store4<E>(dz + tl * a.ldz + vl, tile.acc[i][j][rq * 4], tile.acc[i][j][rq * 4 + 1],
+                      tile.acc[i][j][rq * 4 + 2], tile.acc[i][j][rq * 4 + 3]);
+        }
+    }
   }
+  if constexpr (ESZ == 2) store_dz_tile<TL>(tile, lds, dz, a.ldz, v0 - a.v_begin, a.ldz_cols,
+                                            tl0, a.t_count, wm, wn);
+}
+
+template <typename E>
+__global__ void __launch_bounds__(LogitCfg<E>::T::NT, 1) bwd_dz_kernel(DzArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  int tm, tn;
+  if (!xcd_tile(blockIdx.x, a.n_vtiles, a.n_ttiles, 4, tm, tn)) return;
+  dz_tile<E>(a, tm, tn, lds);
 }
 
 // ================================================================ backward dH
@@ -482,53 +551,61 @@ __global__ void __launch_bounds__(DhCfg<E>::T::NT, 1) bwd_dh_kernel(DhArgs a) {
 }
 
 // ================================================================ backward dW
-// dW[slab] (+)= dZ[block, slab]^T * H[block].  M = slab vocab, N = hidden,
-// K = block tokens.  accumulate: 0 = overwrite, 1 = add to dW (the MFMA
-// accumulators start from the stored dW tile, so the epilogue only stores).
+// dW[slab] (+)= dZ[block, slab]^T * H[block], computed as its transpose
+// H[block]^T * dZ[block, slab]: M = hidden, N = slab vocab, K = block tokens,
+// so that each lane's accumulator quads are four consecutive hidden units of
+// one dW row (16-byte loads and stores).  accumulate: 0 = overwrite, 1 = add
+// to dW (the MFMA accumulators start from the stored dW tile, so the
+// epilogue only stores).
 template <typename E>
 __global__ void __launch_bounds__(DwCfg<E>::T::NT, 1) bwd_dw_kernel(DwArgs a) {
   using TL = typename DwCfg<E>::T;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   constexpr int ESZ = TL::ESZ;
   int tm, tn;
-  if (!xcd_tile(blockIdx.x, a.n_mtiles, a.n_ntiles, 4, tm, tn)) return;
+  if (!xcd_tile(blockIdx.x, a.n_mtiles, a.n_ntiles, 8, tm, tn)) return;
   const int wave = threadIdx.x >> 6;
   const int wm = wave / TL::WN, wn = wave % TL::WN;
-  const int64_t vl0 = (int64_t)tm * TL::BM;  // vocab within slab
-  const int64_t n0 = (int64_t)tn * TL::BN;
+  const int64_t n0 = (int64_t)tm * TL::BM;   // hidden
+  const int64_t vl0 = (int64_t)tn * TL::BN;  // vocab within slab
 
   Operand A, B;
-  A.rs = make_rsrc(a.dz, clamp_bytes((int64_t)a.t_count * a.ldz * ESZ));
-  A.off = (uint32_t)(vl0 * ESZ);
-  A.ld_bytes = (uint32_t)(a.ldz * ESZ);
+  A.rs = make_rsrc(a.H, clamp_bytes(a.T * a.d * ESZ));
+  A.off = (uint32_t)((a.t_begin * a.d + n0) * ESZ);
+  A.ld_bytes = (uint32_t)(a.d * ESZ);
   A.rows = a.t_count;
-  A.cols = (int)min<int64_t>(TL::BM, a.ldz - vl0);
-  B.rs = make_rsrc(a.H, clamp_bytes(a.T * a.d * ESZ));
-  B.off = (uint32_t)((a.t_begin * a.d + n0) * ESZ);
-  B.ld_bytes = (uint32_t)(a.d * ESZ);
+  A.cols = (int)min<int64_t>(TL::BM, a.d - n0);
+  B.rs = make_rsrc(a.dz, clamp_bytes((int64_t)a.t_count * a.ldz * ESZ));
+  B.off = (uint32_t)(vl0 * ESZ);
+  B.ld_bytes = (uint32_t)(a.ldz * ESZ);
   B.rows = a.t_count;
-  B.cols = (int)min<int64_t>(TL::BN, a.d - n0);
+  B.cols = (int)min<int64_t>(TL::BN, a.ldz - vl0);
 
+  const int n_rows = (int)min<int64_t>(TL::BM, a.d - n0);  // a multiple of 8
+  const int v_cols = (int)min<int64_t>(TL::BN, a.v_count - vl0);
+  float* dw = a.dW + (a.v_begin + vl0) * a.d + n0;  // dW row = tile column
   TL tile;
   // token blocks after the first (or a caller's running sum) continue from dW
   if (a.accumulate)
-    tile.load_acc(a.dW + (a.v_begin + vl0) * a.d + n0, a.d,
-                  (int)min<int64_t>(TL::BM, a.v_count - vl0), (int)min<int64_t>(TL::BN, a.d - n0));
+    tile.load_acc_t(dw, a.d, n_rows, v_cols);
   else
     tile.zero();
   tile.mainloop(A, B, a.t_count, lds);
 
+  // each lane holds four consecutive hidden units of one vocab row per quad
 #pragma unroll
   for (int j = 0; j < TL::NI; ++j) {
-    const int64_t n = n0 + TL::col_of(wn, j);
-    if (n >= a.d) continue;
+    const int c = TL::col_of(wn, j);
+    if (c >= v_cols) continue;
 #pragma unroll
     for (int i = 0; i < TL::MI; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t vl = vl0 + TL::row_of(wm, i, r);
-        if (vl >= a.v_count) continue;
-        a.dW[(a.v_begin + vl) * a.d + n] = tile.acc[i][j][r];
+      for (int q = 0; q < 4; ++q) {
+        const int row = TL::row_of(wm, i, 4 * q);
+        if (row < n_rows)
+          *reinterpret_cast<f32x4_t*>(dw + (int64_t)c * a.d + row) =
+              f32x4_t{tile.acc[i][j][4 * q], tile.acc[i][j][4 * q + 1], tile.acc[i][j][4 * q + 2],
+                      tile.acc[i][j][4 * q + 3]};
       }
   }
 }

@@ -73,13 +73,14 @@ struct DwArgs {
   int64_t t_begin;
   int t_count;   // K
   int64_t v_begin;
-  int v_count;   // M
-  int n_mtiles, n_ntiles;
+  int v_count;   // N
+  int n_mtiles, n_ntiles;  // hidden tiles, vocab tiles
   int accumulate;
   float* dW;
 };
 
 struct TileInfo {
+  // logits: vocab x tokens; dH: tokens x hidden; dW: hidden x vocab
   int logit_bm, logit_bn, dh_bm, dh_bn, dw_bm, dw_bn;
 };
 

@@ -114,7 +114,7 @@ struct Tile {
   static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "wave tile must be 32-aligned");
   static_assert(KS >= 1 && BK % KSTEP == 0, "stage must hold whole fragment steps");
   static_assert(KB == 64 || KB == 128, "KC rows of 64 or 128 bytes");
-  static_assert(DMA ? NS >= 3 : NS == 2, "DMA ring of >= 3 stages, or a double buffer");
+  static_assert(DMA ? NS >= 2 : NS == 2, "DMA ring of >= 2 stages, or a register-staged double buffer");
   static constexpr int A_LD = BM * BK / CW / NT;  // 16-byte loads per thread per stage (no DMA)
   static constexpr int B_LD = BN * BK / CW / NT;
   static_assert(DMA || ((BM * BK / CW) % NT == 0 && (BN * BK / CW) % NT == 0), "loads must divide");
@@ -147,6 +147,34 @@ struct Tile {
               float, __builtin_amdgcn_raw_buffer_load_b32(rs, base, __builtin_amdgcn_readfirstlane(soff), 0));
         }
       }
+  }
+
+  // acc = C[tile] for a matrix stored transposed: tile element (row, col) is
+  // c[col * ldc + row], with `rows` x `cols` of the tile valid and `rows` a
+  // multiple of 4.  Each lane's four consecutive rows are one 16-byte load.
+  // The buffer resource ends at the last valid element, so columns past
+  // `cols` read as 0.
+  __device__ __forceinline__ void load_acc_t(const float* c, int64_t ldc, int rows, int cols) {
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int64_t bytes = rows > 0 && cols > 0 ? ((int64_t)(cols - 1) * ldc + rows) * 4 : 0;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(c, (uint32_t)(bytes > 0x7fffffff ? 0x7fffffff : bytes));
+    const uint32_t ld4 = (uint32_t)ldc * 4u;
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+      const uint32_t base = (uint32_t)col_of(wn, j) * ld4;
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = row_of(wm, i, 4 * q);
+          const f32x4_t v = __builtin_bit_cast(
+              f32x4_t, buffer_load16(rs, row < rows ? base + (uint32_t)row * 4u : kOOB));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = v[e];
+        }
+    }
   }
 
   __device__ __forceinline__ void zero() {
@@ -412,8 +440,81 @@ struct Tile {
   //   double-buffered in registers; the last step already reads the first
   //   fragments of stage kt+1.
   __device__ __forceinline__ void mainloop(const Operand& A, const Operand& B, int K, char* lds) {
-    if constexpr (DMA) mainloop_dma(A, B, K, lds);
+    if constexpr (DMA && NS == 2) mainloop_dma2(A, B, K, lds);
+    else if constexpr (DMA) mainloop_dma(A, B, K, lds);
     else mainloop_regs(A, B, K, lds);
+  }
+
+  // DMA into two LDS stages.  Stage kt + 1 is in flight while stage kt is
+  // consumed; after stage kt's last MFMAs: wait for this wave's share of
+  // stage kt + 1, barrier (every share landed, every wave done with stage
+  // kt), issue stage kt + 2 into stage kt's slot, read kt + 1's first
+  // fragments.  The stage's k offset travels in the scalar offset; a chunk's
+  // k bound is only checked on a partial last stage.
+  template <bool KC, int NB, int J>
+  __device__ __forceinline__ static void dma_issue2(const Operand& op, int wave, int k0, bool full,
+                                                    char* dst, const uint32_t* off,
+                                                    const int* krel, const bool* ok) {
+    const uint32_t soff = KC ? (uint32_t)k0 * ESZ : (uint32_t)k0 * op.ld_bytes;
+    const int klim = (KC ? op.cols : op.rows) - k0;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int b = wave + NW * j;
+      if (J * NW == NB || b < NB) {
+        const bool v = ok[j] && (full || krel[j] < klim);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            op.rs, (__attribute__((address_space(3))) void*)(dst + b * 1024), 16,
+            v ? off[j] : kOOB, __builtin_amdgcn_readfirstlane(soff), 0, 0);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void mainloop_dma2(const Operand& A, const Operand& B, int K,
+                                                char* lds) {
+    static_assert(KS % 2 == 0, "fragment sets alternate within a stage");
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int nk = (K + BK - 1) / BK;
+    if (nk <= 0) return;
+    uint32_t offa[A_J], offb[B_J];
+    int ka[A_J], kb[B_J];
+    bool oka[A_J], okb[B_J];
+    dma_setup<A_KC, BM, A_PITCH, A_NB, A_J>(A, wave, offa, ka, oka);
+    dma_setup<B_KC, BN, B_PITCH, B_NB, B_J>(B, wave, offb, kb, okb);
+    // dma_setup's offsets include the operand origin at k = 0
+    auto issue = [&](int t) {
+      char* st = lds + (t & 1) * STAGE;
+      const bool full = (t + 1) * BK <= K;
+      dma_issue2<A_KC, A_NB, A_J>(A, wave, t * BK, full, st, offa, ka, oka);
+      dma_issue2<B_KC, B_NB, B_J>(B, wave, t * BK, full, st + A_BYTES, offb, kb, okb);
+    };
+    issue(0);
+    if (nk > 1) issue(1);
+    if (nk > 1) {
+      const int per_stage = min(A_J, (A_NB - wave + NW - 1) / NW) + min(B_J, (B_NB - wave + NW - 1) / NW);
+      wait_vm(per_stage);
+    } else {
+      wait_vm(0);
+    }
+    asm volatile("s_barrier" ::: "memory");
+    u32x4_t fa[2][MI], fb[2][NI];
+    read_frags(lds, lds + A_BYTES, wm, wn, 0, fa[0], fb[0]);
+    for (int kt = 0; kt < nk; ++kt) {
+      const char* cur = lds + (kt & 1) * STAGE;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) read_frags(cur, cur + A_BYTES, wm, wn, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+        mma_all(fa[ks & 1], fb[ks & 1]);
+      }
+      if (kt + 1 < nk) {
+        wait_vm(0);
+        asm volatile("s_barrier" ::: "memory");
+        if (kt + 2 < nk) issue(kt + 2);
+        const char* nx = lds + ((kt + 1) & 1) * STAGE;
+        read_frags(nx, nx + A_BYTES, wm, wn, 0, fa[0], fb[0]);
+      }
+    }
+    __syncthreads();
   }
 
   // Register-staged double buffer (NS == 2), LDS laid out [A0 A1 B0 B1] so
@@ -553,23 +654,29 @@ struct Tile {
   }
 };
 
-// Workgroup -> tile mapping that keeps the workgroups co-resident on one XCD
-// (consecutive workgroup ids are dealt round-robin over the 8 XCDs, each with
-// its own L2) on a compact block of tiles: XCD x takes a contiguous range of
-// tile ids, and ids are rastered in column strips `group` tiles tall, so the
-// ~32 workgroups an XCD runs at once share a few A and B panels in its L2.
-// Returns false for the few padding workgroups past the last tile.
-__device__ __forceinline__ bool xcd_tile(int bid, int nm, int nn, int group, int& tm, int& tn) {
-  const int total = nm * nn;
-  const int per = (total + 7) / 8;
-  const int id = (bid & 7) * per + (bid >> 3);
-  if (id >= total) return false;
+// Tile id -> (tm, tn): ids are rastered in column strips `group` tiles tall,
+// so that a run of consecutive ids shares a few A (tm) and B (tn) panels.
+__device__ __forceinline__ void raster(int id, int nm, int nn, int group, int& tm, int& tn) {
   const int span = group * nn;
   const int g = id / span, w = id % span;
   const int m0 = g * group;
   const int gs = min(nm - m0, group);
   tm = m0 + w % gs;
   tn = w / gs;
+}
+
+// Workgroup -> tile mapping that keeps the workgroups co-resident on one XCD
+// (consecutive workgroup ids are dealt round-robin over the 8 XCDs, each with
+// its own L2) on a compact block of tiles: XCD x takes a contiguous range of
+// tile ids, rastered as above, so the ~32 workgroups an XCD runs at once
+// share a few A and B panels in its L2.  Returns false for the few padding
+// workgroups past the last tile.
+__device__ __forceinline__ bool xcd_tile(int bid, int nm, int nn, int group, int& tm, int& tn) {
+  const int total = nm * nn;
+  const int per = (total + 7) / 8;
+  const int id = (bid & 7) * per + (bid >> 3);
+  if (id >= total) return false;
+  raster(id, nm, nn, group, tm, tn);
   return true;
 }
 
