@@ -187,6 +187,60 @@ def summarize_traffic(fetch_csv: str, write_csv: str, cfetch_csv: str, cwrite_cs
     }
 
 
+def shard_leg(flce, wl, H, W, cfg, ws, stream, steps: int):
+    """The vocab-parallel path at the same per-GPU shape: W taken as rank 1 of
+    a two-way split of a 2V-id vocabulary (vocab_start = V), targets uniform
+    over all 2V ids, so half fall in this shard.  One step = forward_shard +
+    merge of two shards' statistics (the second shard's row stands in for the
+    gathered one) + backward_shard.  Timed with hipEvents on `stream`."""
+    import numpy as np
+    import torch
+    T, d, V = cfg.T, cfg.d, cfg.V
+    dev = W.device
+    y2 = torch.from_numpy(wl.uniform_targets(np.random.default_rng(cfg.seed_base + 97), T, 2 * V)).to(dev)
+    plan = flce.flce_plan(T, d, V, cfg.dtype)
+    stats = torch.empty((2, 2, T), dtype=torch.float32, device=dev)
+    loss = torch.empty(T, dtype=torch.float32, device=dev)
+    lse = torch.empty(T, dtype=torch.float32, device=dev)
+    dH = torch.empty((T, d), dtype=H.dtype, device=dev)
+    dW = torch.empty((V, d), dtype=torch.float32, device=dev)
+
+    def step():
+        flce.flce_forward_shard(plan, H, W, y2, V, 2 * V, wl.IGNORE_INDEX, lse_shard=stats[0, 1],
+                                zt_shard=stats[1, 1], ws=ws, stream=stream)
+        flce.flce_merge_shards(stats[0], stats[1], y2, 2 * V, wl.IGNORE_INDEX, 1.0, loss=loss,
+                               lse=lse, stream=stream)
+        flce.flce_backward_shard(plan, H, W, y2, lse, V, 2 * V, wl.IGNORE_INDEX, 1.0,
+                                 dH_partial=dH, dW_shard=dW, ws=ws, stream=stream)
+
+    # Stand-in for the other rank's gathered statistics: this shard's lse with
+    # no target logits (tokens whose target lies in the stand-in get a NaN loss;
+    # the merge's cost does not depend on the values).
+    flce.flce_forward_shard(plan, H, W, y2, V, 2 * V, wl.IGNORE_INDEX, lse_shard=stats[0, 0],
+                            zt_shard=stats[1, 0], ws=ws, stream=stream)
+    stats[1, 0].fill_(float("-inf"))
+    step()
+    torch.cuda.synchronize()
+    flce.flce_timing_collect()
+    flce.flce_timing_enable(True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    flce.flce_timing_enable(False)
+    k = flce.flce_timing_collect()
+    ms = e0.elapsed_time(e1) / steps
+    merge = k.get("shard_merge", {"total_ms": 0.0, "launches": 1})
+    log(f"  shard leg: {ms:.2f} ms/step, {8.0 * T * d * V / ms / 1e9:.1f} TFLOP/s")
+    return {"workload": f"{cfg.name} as vocab shard 1 of 2 (vocab_start={V}, vocab_total={2 * V})",
+            "steps": steps, "ms_per_step": round(ms, 3),
+            "tflops": round(8.0 * T * d * V / ms / 1e9, 2),
+            "merge_avg_ms": round(merge["total_ms"] / max(1, merge["launches"]), 4)}
+
+
 def copy_calibration(mib: int):
     """A plain copy of mib MiB (read mib, write mib), three times: the byte
     counters of a profiler run over it give the scale of FETCH_SIZE and
@@ -209,6 +263,9 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3, help="workload index (default 3)")
+    ap.add_argument("--shard-steps", type=int, default=3,
+                    help="steps of the vocab-shard leg: W as rank 1 of 2 of a vocabulary of 2V "
+                         "ids (0 skips it)")
     ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="rows of the CPU-oracle sample (0 skips it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
@@ -316,6 +373,8 @@ def main():
                 "traffic": measured_traffic(dom_name, cfg.name), "flops_per_launch": flops_per_launch,
                 "avg_launch_ms": round(avg_ms, 4), "launches": dom["launches"]}
 
+    shard = shard_leg(flce, wl, H, W, cfg, ws, stream, args.shard_steps) if args.shard_steps > 0 else None
+
     cpu = None
     if args.cpu_rows > 0:
         log(f"cpu baseline: oracle on {args.cpu_rows} rows")
@@ -352,6 +411,7 @@ def main():
                         if v["total_ms"] else 0.0}
                     for k, v in kernels.items()},
         "kernel_ms_per_step": round(step_kernel_ms, 3),
+        "shard_mode": shard,
         "plan": {"fwd_splits": plan.fwd_splits, "bwd_block": plan.bwd_block,
                  "bwd_slab": plan.bwd_slab, "n_blocks": plan.n_blocks, "n_slabs": plan.n_slabs},
     }

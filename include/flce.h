@@ -127,6 +127,65 @@ flce_status_t flce_backward(const flce_plan_t* plan, const void* H, const void* 
                             float grad_scale, void* dH, float* dW, int accumulate_dW, void* ws,
                             uint64_t ws_bytes, void* stream);
 
+/* ---- vocab-parallel shard mode ------------------------------------------
+ * The Megatron-Lite / bumblebee write-up (section 2.3, step 1) runs this loss
+ * vocab-parallel: each of P tensor-parallel ranks holds a contiguous slice of
+ * W's rows.  A shard's forward reduces its own vocab slice to two per-token
+ * statistics; gathering them from all P shards and merging gives the same
+ * loss and lse as the unsharded forward; the backward of each shard then
+ * needs only the merged lse.  The calls below are the per-GPU parts; the
+ * exchange between them (an all-gather of 8 * T bytes per shard, and a sum
+ * of the P partial dH) is the caller's.
+ *
+ * A shard plan is flce_plan(T, d, V_local, ...), V_local the shard's rows;
+ * the shard is vocab ids [vocab_start, vocab_start + V_local) of a vocabulary
+ * of vocab_total ids, and targets y stay global ids.  FLCE_ERR_INVALID_ARG
+ * when vocab_total is outside [1, 2^31) or the shard does not lie inside it.
+ */
+
+/* flce_forward_shard -- per-token statistics of one vocab shard.
+ *   W_shard [V_local x d] : the shard's rows of W, in the plan's dtype.
+ *   lse_shard [T] : float, log sum over the shard's ids of exp(logit).
+ *   zt_shard  [T] : float, the target logit when y lies in the shard, else
+ *                   -inf (also for ignored tokens).
+ *   ws, ws_bytes : as flce_forward (plan->fwd_ws_bytes).
+ * Other arguments and errors as flce_forward. */
+flce_status_t flce_forward_shard(const flce_plan_t* plan, const void* H, const void* W_shard,
+                                 const int64_t* y, int64_t ignore_index, int64_t vocab_start,
+                                 int64_t vocab_total, float* lse_shard, float* zt_shard, void* ws,
+                                 uint64_t ws_bytes, void* stream);
+
+/* flce_merge_shards -- loss and lse from the statistics of n_shards shards.
+ *   lse_shards, zt_shards : device floats [n_shards x T] (shard-major, as an
+ *             all-gather lays them out), each row from flce_forward_shard.
+ *   The merged lse is the log-sum-exp of the shards' lse, in ascending shard
+ *   order; the target logit is the one finite zt.  loss as flce_forward:
+ *   0 for ignored tokens, NaN for targets outside [0, vocab_total) and for
+ *   valid targets that no shard holds; loss_reduced (optional) =
+ *   scale * sum(loss) in a fixed order.  Any shard order gives the same
+ *   result up to rounding; the same order on every rank gives identical bits.
+ * FLCE_ERR_INVALID_ARG for T outside [0, 2^31), n_shards < 1 or above
+ * vocab_total, or NULL buffers when T > 0. */
+flce_status_t flce_merge_shards(int64_t T, int32_t n_shards, const float* lse_shards,
+                                const float* zt_shards, const int64_t* y, int64_t ignore_index,
+                                int64_t vocab_total, float scale, float* loss, float* lse,
+                                float* loss_reduced, void* stream);
+
+/* flce_backward_shard -- one shard's part of dH and its slice of dW.
+ *   lse [T]  : the merged lse over the whole vocabulary.
+ *   dH_partial [T x d] : this shard's term dZ_shard * W_shard, in the plan's
+ *              dtype; dH is the sum of the P partials.
+ *   dW_shard [V_local x d] : float, rows vocab_start.. of dW (overwritten or
+ *              accumulated as flce_backward).
+ * Tokens whose target lies in another shard contribute their softmax only;
+ * the one-hot term lands in the shard that holds the target.  Other
+ * arguments, workspace and errors as flce_backward. */
+flce_status_t flce_backward_shard(const flce_plan_t* plan, const void* H, const void* W_shard,
+                                  const int64_t* y, const float* lse, int64_t ignore_index,
+                                  int64_t vocab_start, int64_t vocab_total, float grad_scale,
+                                  void* dH_partial, float* dW_shard, int accumulate_dW, void* ws,
+                                  uint64_t ws_bytes, void* stream);
+
 /* ---- kernel timing (a profiling aid; off by default) --------------------
  * While enabled, every kernel launch made by flce_forward / flce_backward on
  * the calling process is bracketed by two hipEvents recorded on the caller's

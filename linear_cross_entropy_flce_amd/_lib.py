@@ -22,7 +22,8 @@ FLCE_ERR_UNSUPPORTED = -2
 FLCE_ERR_WORKSPACE = -3
 FLCE_ERR_HIP = -4
 
-EXPORTED = ["flce_plan", "flce_forward", "flce_backward", "flce_timing_enable",
+EXPORTED = ["flce_plan", "flce_forward", "flce_backward", "flce_forward_shard",
+            "flce_merge_shards", "flce_backward_shard", "flce_timing_enable",
             "flce_timing_collect", "flce_status_string", "flce_last_error", "flce_version"]
 
 
@@ -79,6 +80,14 @@ def load(path: str = LIB_PATH):
     lib.flce_forward.restype = ctypes.c_int
     lib.flce_backward.argtypes = [P, vp, vp, vp, vp, i64, f32, vp, vp, ctypes.c_int, vp, u64, vp]
     lib.flce_backward.restype = ctypes.c_int
+    lib.flce_forward_shard.argtypes = [P, vp, vp, vp, i64, i64, i64, vp, vp, vp, u64, vp]
+    lib.flce_forward_shard.restype = ctypes.c_int
+    lib.flce_merge_shards.argtypes = [i64, ctypes.c_int32, vp, vp, vp, i64, i64, f32, vp, vp, vp,
+                                      vp]
+    lib.flce_merge_shards.restype = ctypes.c_int
+    lib.flce_backward_shard.argtypes = [P, vp, vp, vp, vp, i64, i64, i64, f32, vp, vp,
+                                        ctypes.c_int, vp, u64, vp]
+    lib.flce_backward_shard.restype = ctypes.c_int
     lib.flce_timing_enable.argtypes = [ctypes.c_int]
     lib.flce_timing_enable.restype = ctypes.c_int
     lib.flce_timing_collect.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int,
@@ -245,3 +254,84 @@ def flce_backward(plan: Plan, H, W, y, lse, ignore_index: int = -100, grad_scale
                                 1 if accumulate_dW else 0, _ptr(ws),
                                 int(ws.numel() * ws.element_size()), _stream(stream)))
     return dH, dW
+
+
+def flce_forward_shard(plan: Plan, H, W_shard, y, vocab_start: int, vocab_total: int,
+                       ignore_index: int = -100, lse_shard=None, zt_shard=None, ws=None,
+                       stream=None):
+    """flce_forward_shard(): returns (lse_shard, zt_shard) of one vocab shard.
+
+    plan is for the shard (V = its rows); y holds global vocab ids."""
+    import torch
+    T, d, V = plan.T, plan.d, plan.V
+    dev = W_shard.device
+    et = _elem_dtype(plan)
+    _check_tensor("H", H, (T, d), et)
+    _check_tensor("W_shard", W_shard, (V, d), et)
+    _check_tensor("y", y, (T,), torch.int64)
+    if lse_shard is None:
+        lse_shard = torch.empty(T, dtype=torch.float32, device=dev)
+    if zt_shard is None:
+        zt_shard = torch.empty(T, dtype=torch.float32, device=dev)
+    _check_tensor("lse_shard", lse_shard, (T,), torch.float32)
+    _check_tensor("zt_shard", zt_shard, (T,), torch.float32)
+    if ws is None:
+        ws = workspace(plan, dev)
+    _check(load().flce_forward_shard(ctypes.byref(plan), _ptr(H), _ptr(W_shard), _ptr(y),
+                                     int(ignore_index), int(vocab_start), int(vocab_total),
+                                     _ptr(lse_shard), _ptr(zt_shard), _ptr(ws),
+                                     int(ws.numel() * ws.element_size()), _stream(stream)))
+    return lse_shard, zt_shard
+
+
+def flce_merge_shards(lse_shards, zt_shards, y, vocab_total: int, ignore_index: int = -100,
+                      scale: float = 1.0, loss=None, lse=None, loss_reduced=None, stream=None):
+    """flce_merge_shards(): lse_shards, zt_shards [n_shards, T] -> (loss, lse, loss_reduced)."""
+    import torch
+    if lse_shards.dim() != 2:
+        raise ValueError("lse_shards must be [n_shards, T]")
+    P, T = lse_shards.shape
+    dev = lse_shards.device
+    _check_tensor("lse_shards", lse_shards, (P, T), torch.float32)
+    _check_tensor("zt_shards", zt_shards, (P, T), torch.float32)
+    _check_tensor("y", y, (T,), torch.int64)
+    if loss is None:
+        loss = torch.empty(T, dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(T, dtype=torch.float32, device=dev)
+    _check_tensor("loss", loss, (T,), torch.float32)
+    _check_tensor("lse", lse, (T,), torch.float32)
+    _check(load().flce_merge_shards(int(T), int(P), _ptr(lse_shards), _ptr(zt_shards), _ptr(y),
+                                    int(ignore_index), int(vocab_total), float(scale), _ptr(loss),
+                                    _ptr(lse), _ptr(loss_reduced), _stream(stream)))
+    return loss, lse, loss_reduced
+
+
+def flce_backward_shard(plan: Plan, H, W_shard, y, lse, vocab_start: int, vocab_total: int,
+                        ignore_index: int = -100, grad_scale: float = 1.0, dH_partial=None,
+                        dW_shard=None, accumulate_dW: bool = False, ws=None, stream=None):
+    """flce_backward_shard(): returns (dH_partial, dW_shard); lse is the merged one."""
+    import torch
+    T, d, V = plan.T, plan.d, plan.V
+    dev = W_shard.device
+    et = _elem_dtype(plan)
+    _check_tensor("H", H, (T, d), et)
+    _check_tensor("W_shard", W_shard, (V, d), et)
+    _check_tensor("y", y, (T,), torch.int64)
+    _check_tensor("lse", lse, (T,), torch.float32)
+    if dH_partial is None:
+        dH_partial = torch.empty((T, d), dtype=et, device=dev)
+    if dW_shard is None:
+        if accumulate_dW:
+            raise ValueError("accumulate_dW needs an existing dW_shard")
+        dW_shard = torch.empty((V, d), dtype=torch.float32, device=dev)
+    _check_tensor("dH_partial", dH_partial, (T, d), et)
+    _check_tensor("dW_shard", dW_shard, (V, d), torch.float32)
+    if ws is None:
+        ws = workspace(plan, dev)
+    _check(load().flce_backward_shard(ctypes.byref(plan), _ptr(H), _ptr(W_shard), _ptr(y),
+                                      _ptr(lse), int(ignore_index), int(vocab_start),
+                                      int(vocab_total), float(grad_scale), _ptr(dH_partial),
+                                      _ptr(dW_shard), 1 if accumulate_dW else 0, _ptr(ws),
+                                      int(ws.numel() * ws.element_size()), _stream(stream)))
+    return dH_partial, dW_shard

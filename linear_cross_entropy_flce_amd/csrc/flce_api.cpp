@@ -55,9 +55,11 @@ flce_status_t hip_fail(hipError_t e, const char* what) {
 }
 
 // ------------------------------------------------------------ kernel timing
-enum KernelId { K_FWD_SWEEP, K_FWD_MERGE, K_LOSS_SUM, K_BWD_DZ, K_BWD_DH, K_BWD_DW, K_FILL, K_COUNT };
-const char* const kKernelNames[K_COUNT] = {"fwd_sweep", "fwd_merge", "loss_sum", "bwd_dz",
-                                           "bwd_dh",    "bwd_dw",    "fill_zero"};
+enum KernelId {
+  K_FWD_SWEEP, K_FWD_MERGE, K_LOSS_SUM, K_BWD_DZ, K_BWD_DH, K_BWD_DW, K_FILL, K_SHARD_MERGE, K_COUNT
+};
+const char* const kKernelNames[K_COUNT] = {"fwd_sweep", "fwd_merge", "loss_sum",  "bwd_dz",
+                                           "bwd_dh",    "bwd_dw",    "fill_zero", "shard_merge"};
 
 struct TimingRec {
   int kid;
@@ -143,6 +145,215 @@ double backward_cost(int64_t T, int64_t d, int64_t V, int64_t B, int64_t Vs,
     }
   }
   return cost;
+}
+
+}  // namespace
+
+namespace {
+
+flce_status_t check_shard(const flce_plan_t& p, int64_t vocab_start, int64_t vocab_total) {
+  if (vocab_total < 1 || vocab_total >= ((int64_t)1 << 31))
+    return fail(FLCE_ERR_INVALID_ARG, "vocab_total = %lld out of range", (long long)vocab_total);
+  if (vocab_start < 0 || vocab_start > vocab_total - p.V)
+    return fail(FLCE_ERR_INVALID_ARG, "shard [%lld, %lld) is not inside [0, %lld)",
+                (long long)vocab_start, (long long)(vocab_start + p.V), (long long)vocab_total);
+  return ok();
+}
+
+// The forward for one vocab shard (the whole vocabulary when tg.start = 0
+// and tg.total = V).  shard: write the shard statistics (lse of the shard,
+// target logit or -inf) into lse and zt_out instead of loss and lse.
+flce_status_t forward_impl(const flce_plan_t* plan, const void* H, const void* W,
+                           const flce::Targets& tg, float scale, float* loss, float* lse,
+                           float* loss_reduced, float* zt_out, bool shard, void* ws,
+                           uint64_t ws_bytes, void* stream) {
+  flce_status_t st = check_plan(plan);
+  if (st != FLCE_OK) return st;
+  const flce_plan_t& p = *plan;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (!W) return fail(FLCE_ERR_INVALID_ARG, "W is NULL");
+  if (p.T > 0 && (!H || !tg.y || !lse || !ws || (shard ? !zt_out : !loss)))
+    return fail(FLCE_ERR_INVALID_ARG, shard ? "H, y, lse_shard, zt_shard and ws must be non-NULL when T > 0"
+                                            : "H, y, loss, lse and ws must be non-NULL when T > 0");
+  if (misaligned(H) || misaligned(W) || misaligned(ws))
+    return fail(FLCE_ERR_UNSUPPORTED, "H, W and ws must be 16-byte aligned");
+  if (p.T > 0 && ws_bytes < p.fwd_ws_bytes)
+    return fail(FLCE_ERR_WORKSPACE, "forward needs %llu workspace bytes, got %llu",
+                (unsigned long long)p.fwd_ws_bytes, (unsigned long long)ws_bytes);
+  const bool bf16 = p.dtype == FLCE_BF16;
+  hipError_t e;
+  if (p.T == 0) {
+    if (loss_reduced) {
+      Timed tm(s, K_LOSS_SUM, 0, 4);
+      e = flce::launch_loss_sum(loss, 0, scale, loss_reduced, s);
+      tm.done();
+      if (e != hipSuccess) return hip_fail(e, "loss_sum launch");
+    }
+    return ok();
+  }
+  float* part = reinterpret_cast<float*>(ws);
+  float* zt = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
+                                       round_up((int64_t)p.fwd_splits * p.T * 2 * 4, 256));
+  flce::FwdArgs a;
+  a.H = H;
+  a.W = W;
+  a.tg = tg;
+  a.T = p.T;
+  a.d = (int)p.d;
+  a.V = (int)p.V;
+  a.n_ttiles = (int)cdiv(p.T, p.tile_t);
+  a.n_vtiles = (int)cdiv(p.V, p.tile_v);
+  a.splits = p.fwd_splits;
+  a.tps = p.fwd_tiles_per_split;
+  a.grp = p.fwd_splits >= 32 ? 1 : 32 / p.fwd_splits;
+  a.part = part;
+  a.zt = zt;
+  const int64_t per_group = (int64_t)a.grp * a.splits;
+  const int64_t groups = cdiv(a.n_ttiles, a.grp);
+  const int64_t grid = 8 * per_group * cdiv(groups, 8);
+  const double esz = (double)p.elem_bytes;
+  Timed t_sweep(s, K_FWD_SWEEP, 2.0 * p.T * p.d * p.V,
+                (p.T + p.V) * p.d * esz + (double)p.fwd_splits * p.T * 8 + p.T * 12.0);
+  e = flce::launch_fwd_sweep(a, bf16, (int)grid, s);
+  t_sweep.done();
+  if (e != hipSuccess) return hip_fail(e, "forward sweep launch");
+  flce::MergeArgs m;
+  m.part = part;
+  m.zt = zt;
+  m.tg = tg;
+  m.T = p.T;
+  m.V = (int)p.V;
+  m.splits = p.fwd_splits;
+  m.shard = shard ? 1 : 0;
+  m.loss = loss;
+  m.lse = lse;
+  m.zt_out = zt_out;
+  Timed t_merge(s, K_FWD_MERGE, 0, (double)p.fwd_splits * p.T * 8 + p.T * 20.0);
+  e = flce::launch_fwd_merge(m, s);
+  t_merge.done();
+  if (e != hipSuccess) return hip_fail(e, "forward merge launch");
+  if (loss_reduced) {
+    Timed tm(s, K_LOSS_SUM, 0, p.T * 4.0 + 4);
+    e = flce::launch_loss_sum(loss, p.T, scale, loss_reduced, s);
+    tm.done();
+    if (e != hipSuccess) return hip_fail(e, "loss_sum launch");
+  }
+  return ok();
+}
+
+// The backward for one vocab shard (the whole vocabulary when tg.start = 0
+// and tg.total = V); lse is over the whole vocabulary.
+flce_status_t backward_impl(const flce_plan_t* plan, const void* H, const void* W,
+                            const flce::Targets& tg, const float* lse, float grad_scale, void* dH,
+                            float* dW, int accumulate_dW, void* ws, uint64_t ws_bytes,
+                            void* stream) {
+  flce_status_t st = check_plan(plan);
+  if (st != FLCE_OK) return st;
+  const flce_plan_t& p = *plan;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (!W || !dW) return fail(FLCE_ERR_INVALID_ARG, "W and dW must be non-NULL");
+  if (p.T > 0 && (!H || !tg.y || !lse || !dH || !ws))
+    return fail(FLCE_ERR_INVALID_ARG, "H, y, lse, dH and ws must be non-NULL when T > 0");
+  if (misaligned(H) || misaligned(W) || misaligned(dH) || misaligned(dW) || misaligned(ws))
+    return fail(FLCE_ERR_UNSUPPORTED, "H, W, dH, dW and ws must be 16-byte aligned");
+  if (p.T > 0 && ws_bytes < p.bwd_ws_bytes)
+    return fail(FLCE_ERR_WORKSPACE, "backward needs %llu workspace bytes, got %llu",
+                (unsigned long long)p.bwd_ws_bytes, (unsigned long long)ws_bytes);
+  const bool bf16 = p.dtype == FLCE_BF16;
+  const flce::TileInfo ti = flce::tile_info(bf16);
+  hipError_t e;
+  if (p.T == 0) {
+    if (!accumulate_dW) {
+      Timed tm(s, K_FILL, 0, p.V * p.d * 4.0);
+      e = flce::launch_fill_zero(dW, p.V * p.d, s);
+      tm.done();
+      if (e != hipSuccess) return hip_fail(e, "dW fill launch");
+    }
+    return ok();
+  }
+  void* dz = ws;
+  float* dh_acc = p.dh_acc_bytes ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
+                                                            p.dz_ws_bytes)
+                                 : nullptr;
+  for (int64_t b = 0; b < p.n_blocks; ++b) {
+    const int64_t t_begin = b * p.bwd_block;
+    const int t_count = (int)(p.T - t_begin < p.bwd_block ? p.T - t_begin : p.bwd_block);
+    for (int64_t sl = 0; sl < p.n_slabs; ++sl) {
+      const int64_t v_begin = sl * p.bwd_slab;
+      const int v_count = (int)(p.V - v_begin < p.bwd_slab ? p.V - v_begin : p.bwd_slab);
+
+      flce::DzArgs z;
+      z.H = H;
+      z.W = W;
+      z.tg = tg;
+      z.lse = lse;
+      z.T = p.T;
+      z.d = (int)p.d;
+      z.V = (int)p.V;
+      z.t_begin = t_begin;
+      z.t_count = t_count;
+      z.v_begin = v_begin;
+      z.n_vtiles = (int)cdiv(v_count, ti.logit_bm);
+      z.n_ttiles = (int)cdiv(t_count, ti.logit_bn);
+      z.ldz = p.bwd_slab;
+      z.ldz_cols = (int64_t)z.n_vtiles * ti.logit_bm;
+      z.grad_scale = grad_scale;
+      z.dz = dz;
+      const double esz = (double)p.elem_bytes;
+      const double tc = t_count, vc = v_count, dd = (double)p.d;
+      Timed t_dz(s, K_BWD_DZ, 2.0 * tc * dd * vc, (tc + vc) * dd * esz + tc * 12 + tc * vc * esz);
+      e = flce::launch_bwd_dz(z, bf16, s);
+      t_dz.done();
+      if (e != hipSuccess) return hip_fail(e, "dZ launch");
+
+      flce::DhArgs h;
+      h.dz = dz;
+      h.W = W;
+      h.ldz = p.bwd_slab;
+      h.d = (int)p.d;
+      h.V = (int)p.V;
+      h.t_begin = t_begin;
+      h.t_count = t_count;
+      h.v_begin = v_begin;
+      h.k_count = v_count;
+      h.n_mtiles = (int)cdiv(t_count, ti.dh_bm);
+      h.n_ntiles = (int)cdiv(p.d, ti.dh_bn);
+      if (p.n_slabs == 1) h.mode = 3;
+      else if (sl == 0) h.mode = 0;
+      else if (sl + 1 < p.n_slabs) h.mode = 1;
+      else h.mode = 2;
+      h.dh_acc = dh_acc;
+      h.dH = dH;
+      Timed t_dh(s, K_BWD_DH, 2.0 * tc * dd * vc,
+                 tc * vc * esz + vc * dd * esz +
+                     tc * dd * (h.mode == 1 || h.mode == 2 ? 4.0 : 0.0) +
+                     tc * dd * (h.mode >= 2 ? esz : 4.0));
+      e = flce::launch_bwd_dh(h, bf16, s);
+      t_dh.done();
+      if (e != hipSuccess) return hip_fail(e, "dH launch");
+
+      flce::DwArgs w;
+      w.dz = dz;
+      w.H = H;
+      w.ldz = p.bwd_slab;
+      w.T = p.T;
+      w.d = (int)p.d;
+      w.t_begin = t_begin;
+      w.t_count = t_count;
+      w.v_begin = v_begin;
+      w.v_count = v_count;
+      w.n_mtiles = (int)cdiv(p.d, ti.dw_bm);
+      w.n_ntiles = (int)cdiv(v_count, ti.dw_bn);
+      w.accumulate = (b > 0 || accumulate_dW) ? 1 : 0;
+      w.dW = dW;
+      Timed t_dw(s, K_BWD_DW, 2.0 * tc * dd * vc,
+                 tc * vc * esz + tc * dd * esz + vc * dd * (w.accumulate ? 8.0 : 4.0));
+      e = flce::launch_bwd_dw(w, bf16, s);
+      t_dw.done();
+      if (e != hipSuccess) return hip_fail(e, "dW launch");
+    }
+  }
+  return ok();
 }
 
 }  // namespace
@@ -295,191 +506,87 @@ flce_status_t flce_plan(int64_t T, int64_t d, int64_t V, flce_dtype_t dtype, uin
 flce_status_t flce_forward(const flce_plan_t* plan, const void* H, const void* W, const int64_t* y,
                            int64_t ignore_index, float scale, float* loss, float* lse,
                            float* loss_reduced, void* ws, uint64_t ws_bytes, void* stream) {
-  flce_status_t st = check_plan(plan);
+  const flce_status_t st = check_plan(plan);
   if (st != FLCE_OK) return st;
-  const flce_plan_t& p = *plan;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (!W) return fail(FLCE_ERR_INVALID_ARG, "W is NULL");
-  if (p.T > 0 && (!H || !y || !loss || !lse || !ws))
-    return fail(FLCE_ERR_INVALID_ARG, "H, y, loss, lse and ws must be non-NULL when T > 0");
-  if (misaligned(H) || misaligned(W) || misaligned(ws))
-    return fail(FLCE_ERR_UNSUPPORTED, "H, W and ws must be 16-byte aligned");
-  if (p.T > 0 && ws_bytes < p.fwd_ws_bytes)
-    return fail(FLCE_ERR_WORKSPACE, "forward needs %llu workspace bytes, got %llu",
-                (unsigned long long)p.fwd_ws_bytes, (unsigned long long)ws_bytes);
-  const bool bf16 = p.dtype == FLCE_BF16;
-  hipError_t e;
-  if (p.T == 0) {
-    if (loss_reduced) {
-      Timed tm(s, K_LOSS_SUM, 0, 4);
-      e = flce::launch_loss_sum(loss, 0, scale, loss_reduced, s);
-      tm.done();
-      if (e != hipSuccess) return hip_fail(e, "loss_sum launch");
-    }
-    return ok();
-  }
-  float* part = reinterpret_cast<float*>(ws);
-  float* zt = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
-                                       round_up((int64_t)p.fwd_splits * p.T * 2 * 4, 256));
-  flce::FwdArgs a;
-  a.H = H;
-  a.W = W;
-  a.y = y;
-  a.ignore_index = ignore_index;
-  a.T = p.T;
-  a.d = (int)p.d;
-  a.V = (int)p.V;
-  a.n_ttiles = (int)cdiv(p.T, p.tile_t);
-  a.n_vtiles = (int)cdiv(p.V, p.tile_v);
-  a.splits = p.fwd_splits;
-  a.tps = p.fwd_tiles_per_split;
-  a.grp = p.fwd_splits >= 32 ? 1 : 32 / p.fwd_splits;
-  a.part = part;
-  a.zt = zt;
-  const int64_t per_group = (int64_t)a.grp * a.splits;
-  const int64_t groups = cdiv(a.n_ttiles, a.grp);
-  const int64_t grid = 8 * per_group * cdiv(groups, 8);
-  const double esz = (double)p.elem_bytes;
-  Timed t_sweep(s, K_FWD_SWEEP, 2.0 * p.T * p.d * p.V,
-                (p.T + p.V) * p.d * esz + (double)p.fwd_splits * p.T * 8 + p.T * 12.0);
-  e = flce::launch_fwd_sweep(a, bf16, (int)grid, s);
-  t_sweep.done();
-  if (e != hipSuccess) return hip_fail(e, "forward sweep launch");
-  flce::MergeArgs m;
-  m.part = part;
-  m.zt = zt;
-  m.y = y;
-  m.ignore_index = ignore_index;
-  m.T = p.T;
-  m.V = (int)p.V;
-  m.splits = p.fwd_splits;
-  m.loss = loss;
-  m.lse = lse;
-  Timed t_merge(s, K_FWD_MERGE, 0, (double)p.fwd_splits * p.T * 8 + p.T * 20.0);
-  e = flce::launch_fwd_merge(m, s);
-  t_merge.done();
-  if (e != hipSuccess) return hip_fail(e, "forward merge launch");
-  if (loss_reduced) {
-    Timed tm(s, K_LOSS_SUM, 0, p.T * 4.0 + 4);
-    e = flce::launch_loss_sum(loss, p.T, scale, loss_reduced, s);
-    tm.done();
-    if (e != hipSuccess) return hip_fail(e, "loss_sum launch");
-  }
-  return ok();
+  const flce::Targets tg{y, ignore_index, 0, plan->V};
+  return forward_impl(plan, H, W, tg, scale, loss, lse, loss_reduced, nullptr, false, ws, ws_bytes,
+                      stream);
 }
 
 flce_status_t flce_backward(const flce_plan_t* plan, const void* H, const void* W, const int64_t* y,
                             const float* lse, int64_t ignore_index, float grad_scale, void* dH,
                             float* dW, int accumulate_dW, void* ws, uint64_t ws_bytes,
                             void* stream) {
+  const flce_status_t st = check_plan(plan);
+  if (st != FLCE_OK) return st;
+  const flce::Targets tg{y, ignore_index, 0, plan->V};
+  return backward_impl(plan, H, W, tg, lse, grad_scale, dH, dW, accumulate_dW, ws, ws_bytes,
+                       stream);
+}
+
+flce_status_t flce_forward_shard(const flce_plan_t* plan, const void* H, const void* W_shard,
+                                 const int64_t* y, int64_t ignore_index, int64_t vocab_start,
+                                 int64_t vocab_total, float* lse_shard, float* zt_shard, void* ws,
+                                 uint64_t ws_bytes, void* stream) {
   flce_status_t st = check_plan(plan);
   if (st != FLCE_OK) return st;
-  const flce_plan_t& p = *plan;
+  st = check_shard(*plan, vocab_start, vocab_total);
+  if (st != FLCE_OK) return st;
+  const flce::Targets tg{y, ignore_index, vocab_start, vocab_total};
+  return forward_impl(plan, H, W_shard, tg, 1.f, nullptr, lse_shard, nullptr, zt_shard, true, ws,
+                      ws_bytes, stream);
+}
+
+flce_status_t flce_merge_shards(int64_t T, int32_t n_shards, const float* lse_shards,
+                                const float* zt_shards, const int64_t* y, int64_t ignore_index,
+                                int64_t vocab_total, float scale, float* loss, float* lse,
+                                float* loss_reduced, void* stream) {
+  if (T < 0 || T >= ((int64_t)1 << 31)) return fail(FLCE_ERR_INVALID_ARG, "T = %lld out of range", (long long)T);
+  if (n_shards < 1) return fail(FLCE_ERR_INVALID_ARG, "n_shards = %d must be >= 1", (int)n_shards);
+  if (vocab_total < 1 || vocab_total >= ((int64_t)1 << 31))
+    return fail(FLCE_ERR_INVALID_ARG, "vocab_total = %lld out of range", (long long)vocab_total);
+  if ((int64_t)n_shards > vocab_total)
+    return fail(FLCE_ERR_INVALID_ARG, "%d shards of a %lld-id vocabulary", (int)n_shards,
+                (long long)vocab_total);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (!W || !dW) return fail(FLCE_ERR_INVALID_ARG, "W and dW must be non-NULL");
-  if (p.T > 0 && (!H || !y || !lse || !dH || !ws))
-    return fail(FLCE_ERR_INVALID_ARG, "H, y, lse, dH and ws must be non-NULL when T > 0");
-  if (misaligned(H) || misaligned(W) || misaligned(dH) || misaligned(dW) || misaligned(ws))
-    return fail(FLCE_ERR_UNSUPPORTED, "H, W, dH, dW and ws must be 16-byte aligned");
-  if (p.T > 0 && ws_bytes < p.bwd_ws_bytes)
-    return fail(FLCE_ERR_WORKSPACE, "backward needs %llu workspace bytes, got %llu",
-                (unsigned long long)p.bwd_ws_bytes, (unsigned long long)ws_bytes);
-  const bool bf16 = p.dtype == FLCE_BF16;
-  const flce::TileInfo ti = flce::tile_info(bf16);
+  if (T > 0 && (!lse_shards || !zt_shards || !y || !loss || !lse))
+    return fail(FLCE_ERR_INVALID_ARG, "lse_shards, zt_shards, y, loss and lse must be non-NULL when T > 0");
   hipError_t e;
-  if (p.T == 0) {
-    if (!accumulate_dW) {
-      Timed tm(s, K_FILL, 0, p.V * p.d * 4.0);
-      e = flce::launch_fill_zero(dW, p.V * p.d, s);
-      tm.done();
-      if (e != hipSuccess) return hip_fail(e, "dW fill launch");
-    }
-    return ok();
+  if (T > 0) {
+    flce::ShardMergeArgs m;
+    m.lse_shards = lse_shards;
+    m.zt_shards = zt_shards;
+    m.tg = flce::Targets{y, ignore_index, 0, vocab_total};
+    m.T = T;
+    m.n_shards = n_shards;
+    m.loss = loss;
+    m.lse = lse;
+    Timed tm(s, K_SHARD_MERGE, 0, (double)n_shards * T * 8 + T * 16.0);
+    e = flce::launch_shard_merge(m, s);
+    tm.done();
+    if (e != hipSuccess) return hip_fail(e, "shard merge launch");
   }
-  void* dz = ws;
-  float* dh_acc = p.dh_acc_bytes ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
-                                                            p.dz_ws_bytes)
-                                 : nullptr;
-  for (int64_t b = 0; b < p.n_blocks; ++b) {
-    const int64_t t_begin = b * p.bwd_block;
-    const int t_count = (int)(p.T - t_begin < p.bwd_block ? p.T - t_begin : p.bwd_block);
-    for (int64_t sl = 0; sl < p.n_slabs; ++sl) {
-      const int64_t v_begin = sl * p.bwd_slab;
-      const int v_count = (int)(p.V - v_begin < p.bwd_slab ? p.V - v_begin : p.bwd_slab);
-
-      flce::DzArgs z;
-      z.H = H;
-      z.W = W;
-      z.y = y;
-      z.lse = lse;
-      z.ignore_index = ignore_index;
-      z.T = p.T;
-      z.d = (int)p.d;
-      z.V = (int)p.V;
-      z.t_begin = t_begin;
-      z.t_count = t_count;
-      z.v_begin = v_begin;
-      z.n_vtiles = (int)cdiv(v_count, ti.logit_bm);
-      z.n_ttiles = (int)cdiv(t_count, ti.logit_bn);
-      z.ldz = p.bwd_slab;
-      z.ldz_cols = (int64_t)z.n_vtiles * ti.logit_bm;
-      z.grad_scale = grad_scale;
-      z.dz = dz;
-      const double esz = (double)p.elem_bytes;
-      const double tc = t_count, vc = v_count, dd = (double)p.d;
-      Timed t_dz(s, K_BWD_DZ, 2.0 * tc * dd * vc, (tc + vc) * dd * esz + tc * 12 + tc * vc * esz);
-      e = flce::launch_bwd_dz(z, bf16, s);
-      t_dz.done();
-      if (e != hipSuccess) return hip_fail(e, "dZ launch");
-
-      flce::DhArgs h;
-      h.dz = dz;
-      h.W = W;
-      h.ldz = p.bwd_slab;
-      h.d = (int)p.d;
-      h.V = (int)p.V;
-      h.t_begin = t_begin;
-      h.t_count = t_count;
-      h.v_begin = v_begin;
-      h.k_count = v_count;
-      h.n_mtiles = (int)cdiv(t_count, ti.dh_bm);
-      h.n_ntiles = (int)cdiv(p.d, ti.dh_bn);
-      if (p.n_slabs == 1) h.mode = 3;
-      else if (sl == 0) h.mode = 0;
-      else if (sl + 1 < p.n_slabs) h.mode = 1;
-      else h.mode = 2;
-      h.dh_acc = dh_acc;
-      h.dH = dH;
-      Timed t_dh(s, K_BWD_DH, 2.0 * tc * dd * vc,
-                 tc * vc * esz + vc * dd * esz +
-                     tc * dd * (h.mode == 1 || h.mode == 2 ? 4.0 : 0.0) +
-                     tc * dd * (h.mode >= 2 ? esz : 4.0));
-      e = flce::launch_bwd_dh(h, bf16, s);
-      t_dh.done();
-      if (e != hipSuccess) return hip_fail(e, "dH launch");
-
-      flce::DwArgs w;
-      w.dz = dz;
-      w.H = H;
-      w.ldz = p.bwd_slab;
-      w.T = p.T;
-      w.d = (int)p.d;
-      w.t_begin = t_begin;
-      w.t_count = t_count;
-      w.v_begin = v_begin;
-      w.v_count = v_count;
-      w.n_mtiles = (int)cdiv(p.d, ti.dw_bm);
-      w.n_ntiles = (int)cdiv(v_count, ti.dw_bn);
-      w.accumulate = (b > 0 || accumulate_dW) ? 1 : 0;
-      w.dW = dW;
-      Timed t_dw(s, K_BWD_DW, 2.0 * tc * dd * vc,
-                 tc * vc * esz + tc * dd * esz + vc * dd * (w.accumulate ? 8.0 : 4.0));
-      e = flce::launch_bwd_dw(w, bf16, s);
-      t_dw.done();
-      if (e != hipSuccess) return hip_fail(e, "dW launch");
-    }
+  if (loss_reduced) {
+    Timed tm(s, K_LOSS_SUM, 0, T * 4.0 + 4);
+    e = flce::launch_loss_sum(loss, T, scale, loss_reduced, s);
+    tm.done();
+    if (e != hipSuccess) return hip_fail(e, "loss_sum launch");
   }
   return ok();
+}
+
+flce_status_t flce_backward_shard(const flce_plan_t* plan, const void* H, const void* W_shard,
+                                  const int64_t* y, const float* lse, int64_t ignore_index,
+                                  int64_t vocab_start, int64_t vocab_total, float grad_scale,
+                                  void* dH_partial, float* dW_shard, int accumulate_dW, void* ws,
+                                  uint64_t ws_bytes, void* stream) {
+  flce_status_t st = check_plan(plan);
+  if (st != FLCE_OK) return st;
+  st = check_shard(*plan, vocab_start, vocab_total);
+  if (st != FLCE_OK) return st;
+  const flce::Targets tg{y, ignore_index, vocab_start, vocab_total};
+  return backward_impl(plan, H, W_shard, tg, lse, grad_scale, dH_partial, dW_shard, accumulate_dW,
+                       ws, ws_bytes, stream);
 }
 
 }  // extern "C"

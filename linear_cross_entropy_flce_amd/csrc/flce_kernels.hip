@@ -128,12 +128,16 @@ __device__ __forceinline__ uint32_t clamp_bytes(int64_t b) {
   return (uint32_t)(b < 0 ? 0 : (b > 0x7fffffffLL ? 0x7fffffffLL : b));
 }
 
-// Target of token t as an int in [0, V), or -1 when ignored, -2 when invalid.
-__device__ __forceinline__ int target_code(const int64_t* y, int64_t t, int64_t ignore, int V) {
-  const int64_t v = y[t];
-  if (v == ignore) return -1;
-  if (v < 0 || v >= V) return -2;
-  return (int)v;
+// Target of token t: its row in this vocab shard, in [0, V); or -1 when the
+// token is ignored, -2 when the target is outside [0, total) (invalid), -3
+// when it is valid but belongs to another shard.
+constexpr int kIgnored = -1, kInvalid = -2, kElsewhere = -3;
+__device__ __forceinline__ int target_code(const Targets& g, int64_t t, int V) {
+  const int64_t v = g.y[t];
+  if (v == g.ignore_index) return kIgnored;
+  if (v < 0 || v >= g.total) return kInvalid;
+  const int64_t r = v - g.start;
+  return r >= 0 && r < V ? (int)r : kElsewhere;
 }
 
 // ============================================================== forward sweep
@@ -186,7 +190,7 @@ __global__ void __launch_bounds__(LogitCfg<E>::T::NT, 1)
     m_run[j] = kNegInf;
     s_run[j] = 0.f;
     const int64_t t = t0 + TL::col_of(wn, j);
-    tgt[j] = t < a.T ? target_code(a.y, t, a.ignore_index, a.V) : -1;
+    tgt[j] = t < a.T ? target_code(a.tg, t, a.V) : kIgnored;
   }
 
   TL tile;
@@ -307,11 +311,39 @@ __global__ void __launch_bounds__(256) fwd_merge_kernel(MergeArgs a) {
   }
   const float lse = M + logf(S);
   a.lse[t] = lse;
-  const int code = target_code(a.y, t, a.ignore_index, a.V);
+  const int code = target_code(a.tg, t, a.V);
+  if (a.shard) {
+    a.zt_out[t] = code >= 0 ? a.zt[t] : kNegInf;
+    return;
+  }
   float loss;
-  if (code == -1) loss = 0.f;
-  else if (code == -2) loss = __builtin_nanf("");
+  if (code == kIgnored) loss = 0.f;
+  else if (code < 0) loss = __builtin_nanf("");  // invalid (no other shards here)
   else loss = lse - a.zt[t];
+  a.loss[t] = loss;
+}
+
+// =============================================================== shard merge
+// Per token: lse = log-sum-exp of the shards' lse in ascending shard order;
+// the target logit is the one shard value that is not -inf.  A valid token
+// whose target no shard holds gets a NaN loss.
+__global__ void __launch_bounds__(256) shard_merge_kernel(ShardMergeArgs a) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= a.T) return;
+  float M = kNegInf, zt = kNegInf;
+  for (int p = 0; p < a.n_shards; ++p) {
+    M = fmaxf(M, a.lse_shards[(int64_t)p * a.T + t]);
+    zt = fmaxf(zt, a.zt_shards[(int64_t)p * a.T + t]);
+  }
+  float S = 0.f;
+  for (int p = 0; p < a.n_shards; ++p) S += expf(a.lse_shards[(int64_t)p * a.T + t] - M);
+  const float lse = M + logf(S);
+  a.lse[t] = lse;
+  const int64_t v = a.tg.y[t];
+  float loss;
+  if (v == a.tg.ignore_index) loss = 0.f;
+  else if (v < 0 || v >= a.tg.total || zt == kNegInf) loss = __builtin_nanf("");
+  else loss = lse - zt;
   a.loss[t] = loss;
 }
 
@@ -430,10 +462,10 @@ __device__ __forceinline__ void dz_tile(const DzArgs& a, int tm, int tn, char* l
     const int64_t tl = tl0 + c;
     const bool col_ok = tl < a.t_count;
     const int64_t t = a.t_begin + (col_ok ? tl : 0);
-    const int code = target_code(a.y, t, a.ignore_index, a.V);
+    const int code = target_code(a.tg, t, a.V);
     const float lse_t = a.lse[t];
-    const float bias = code == -1 ? kNegInf
-                       : code == -2 ? __builtin_nanf("")
+    const float bias = code == kIgnored ? kNegInf
+                       : code == kInvalid ? __builtin_nanf("")
                                     : log2g - lse_t * kLog2e;
     // the sign of g is uniform: two copies of the loop keep it out of the
     // per-element work
@@ -656,6 +688,10 @@ hipError_t launch_fwd_merge(const MergeArgs& a, hipStream_t s) {
 hipError_t launch_loss_sum(const float* loss, int64_t T, float scale, float* out, hipStream_t s) {
   hipLaunchKernelGGL(loss_sum_kernel, dim3(1), dim3(1024), 0, s, loss, T, scale, out);
   return hipGetLastError();
+}
+
+hipError_t launch_shard_merge(const ShardMergeArgs& a, hipStream_t s) {
+  return launch(shard_merge_kernel, (int)((a.T + 255) / 256), 256, 0, s, a);
 }
 
 hipError_t launch_bwd_dz(const DzArgs& a, bool bf16, hipStream_t s) {

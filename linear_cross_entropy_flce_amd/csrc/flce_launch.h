@@ -7,11 +7,19 @@
 
 namespace flce {
 
+// Targets of the tokens, as seen by one vocab shard [start, start + V) of a
+// vocabulary of `total` ids (start = 0 and total = V when unsharded).
+struct Targets {
+  const int64_t* y;
+  int64_t ignore_index;
+  int64_t start;
+  int64_t total;
+};
+
 struct FwdArgs {
   const void* H;
   const void* W;
-  const int64_t* y;
-  int64_t ignore_index;
+  Targets tg;
   int64_t T;
   int d, V;
   int n_ttiles, n_vtiles;
@@ -23,10 +31,25 @@ struct FwdArgs {
 struct MergeArgs {
   const float* part;
   const float* zt;
-  const int64_t* y;
-  int64_t ignore_index;
+  Targets tg;
   int64_t T;
   int V, splits;
+  // unsharded: loss [T] and lse [T].  Shard statistics (shard != 0): lse of
+  // the shard's vocab into `lse`, the target logit (or -inf when the target
+  // is not in the shard or ignored) into `zt_out`; `loss` is unused.
+  int shard;
+  float* loss;
+  float* lse;
+  float* zt_out;
+};
+
+// Merge of per-shard statistics [n_shards][T] into loss and lse.
+struct ShardMergeArgs {
+  const float* lse_shards;
+  const float* zt_shards;
+  Targets tg;
+  int64_t T;
+  int n_shards;
   float* loss;
   float* lse;
 };
@@ -34,9 +57,8 @@ struct MergeArgs {
 struct DzArgs {
   const void* H;
   const void* W;
-  const int64_t* y;
+  Targets tg;
   const float* lse;
-  int64_t ignore_index;
   int64_t T;
   int d, V;
   int64_t t_begin;  // first token of the block
@@ -92,5 +114,6 @@ hipError_t launch_bwd_dz(const DzArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_dh(const DhArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_dw(const DwArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+hipError_t launch_shard_merge(const ShardMergeArgs& a, hipStream_t s);
 
 }  // namespace flce

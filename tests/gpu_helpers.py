@@ -95,3 +95,43 @@ def compare(got, ref, dtype, what=("loss", "lse", "dH", "dW"), rows=None):
         errs["dW"] = rel_fro(got["dW"], ref["dW"])
         assert errs["dW"] <= tol["grad"], errs
     return errs
+
+
+def run_gpu_shards(inp: wl.Inputs, bounds, loss_scale=1.0, grad_scale=1.0, merge=None,
+                   backward=True, dev=None):
+    """The vocab-parallel path on one GPU: W's rows cut at `bounds` (ascending
+    vocab ids, 0 .. V), each shard through flce_forward_shard, the statistics
+    stacked as an all-gather would, merged by flce_merge_shards (over the
+    shard indices in `merge`, default all in order), then flce_backward_shard
+    per shard with the merged lse.  dH is the sum of the shards' partials
+    (what the caller's all-reduce does), dW the concatenation of the slices."""
+    H, W, y = dev if dev is not None else device_inputs(inp)
+    V = inp.V
+    shards = list(zip(bounds[:-1], bounds[1:]))
+    merge = list(range(len(shards))) if merge is None else list(merge)
+    plans, stats = [], []
+    for (a, b) in shards:
+        plan = flce.flce_plan(inp.T, inp.d, b - a, inp.dtype)
+        ws = flce.workspace(plan, W.device)
+        lse_s, zt_s = flce.flce_forward_shard(plan, H, W[a:b], y, a, V, inp.ignore_index, ws=ws)
+        plans.append((plan, ws))
+        stats.append((lse_s, zt_s))
+    lse_all = torch.stack([stats[i][0] for i in merge]).contiguous()
+    zt_all = torch.stack([stats[i][1] for i in merge]).contiguous()
+    red = torch.empty(1, dtype=torch.float32, device=W.device)
+    loss, lse, _ = flce.flce_merge_shards(lse_all, zt_all, y, V, inp.ignore_index, loss_scale,
+                                          loss_reduced=red)
+    out = dict(loss=loss, lse=lse, red=red,
+               lse_shards=torch.stack([s[0] for s in stats]),
+               zt_shards=torch.stack([s[1] for s in stats]))
+    if backward:
+        dH = None
+        dWs = []
+        for (a, b), (plan, ws) in zip(shards, plans):
+            dHp, dWp = flce.flce_backward_shard(plan, H, W[a:b], y, lse, a, V, inp.ignore_index,
+                                                grad_scale, ws=ws)
+            dH = dHp.float() if dH is None else dH + dHp.float()
+            dWs.append(dWp)
+        out.update(dH=dH, dW=torch.cat(dWs, 0))
+    torch.cuda.synchronize()
+    return {k: v.float().cpu().numpy() for k, v in out.items()}

@@ -166,3 +166,52 @@ def test_backward_validation(lib):
     assert _bwd(lib, p, lse=None) == flce.FLCE_ERR_INVALID_ARG
     assert _bwd(lib, p, dW=20) == flce.FLCE_ERR_UNSUPPORTED
     assert _bwd(lib, p, ws_bytes=p.bwd_ws_bytes - 1) == flce.FLCE_ERR_WORKSPACE
+
+
+def _fwd_shard(lib, plan, start, total, H=16, W=16, y=16, lse=16, zt=16, ws=16, ws_bytes=1 << 40):
+    return lib.flce_forward_shard(ctypes.byref(plan), H, W, y, -100, start, total, lse, zt, ws,
+                                  ws_bytes, None)
+
+
+def test_forward_shard_validation(lib):
+    p = flce.flce_plan(100, 64, 1000, "bf16")          # a shard of 1000 rows
+    assert _fwd_shard(lib, flce.Plan(), 0, 2000) == flce.FLCE_ERR_INVALID_ARG
+    assert _fwd_shard(lib, p, -1, 2000) == flce.FLCE_ERR_INVALID_ARG       # starts before 0
+    assert _fwd_shard(lib, p, 1001, 2000) == flce.FLCE_ERR_INVALID_ARG     # ends past the vocab
+    assert _fwd_shard(lib, p, 0, 999) == flce.FLCE_ERR_INVALID_ARG         # vocab smaller than shard
+    assert _fwd_shard(lib, p, 0, 1 << 31) == flce.FLCE_ERR_INVALID_ARG     # vocab ids beyond int32
+    assert _fwd_shard(lib, p, 0, 2000, zt=None) == flce.FLCE_ERR_INVALID_ARG
+    assert _fwd_shard(lib, p, 0, 2000, lse=None) == flce.FLCE_ERR_INVALID_ARG
+    assert _fwd_shard(lib, p, 0, 2000, W=24) == flce.FLCE_ERR_UNSUPPORTED
+    assert _fwd_shard(lib, p, 1000, 2000, ws_bytes=p.fwd_ws_bytes - 1) == flce.FLCE_ERR_WORKSPACE
+
+
+def _merge(lib, T=100, P=2, lse=16, zt=16, y=16, total=2000, loss=16, out_lse=16):
+    return lib.flce_merge_shards(T, P, lse, zt, y, -100, total, 1.0, loss, out_lse, None, None)
+
+
+def test_merge_shards_validation(lib):
+    assert _merge(lib, T=-1) == flce.FLCE_ERR_INVALID_ARG
+    assert _merge(lib, P=0) == flce.FLCE_ERR_INVALID_ARG
+    assert _merge(lib, P=3, total=2) == flce.FLCE_ERR_INVALID_ARG           # more shards than ids
+    assert _merge(lib, total=0) == flce.FLCE_ERR_INVALID_ARG
+    assert _merge(lib, zt=None) == flce.FLCE_ERR_INVALID_ARG
+    assert _merge(lib, loss=None) == flce.FLCE_ERR_INVALID_ARG
+    # T == 0 with no reduced loss launches nothing and succeeds without buffers
+    assert _merge(lib, T=0, lse=None, zt=None, y=None, loss=None, out_lse=None) == flce.FLCE_OK
+
+
+def _bwd_shard(lib, plan, start, total, H=16, W=16, y=16, lse=16, dH=16, dW=16, ws=16,
+               ws_bytes=1 << 40):
+    return lib.flce_backward_shard(ctypes.byref(plan), H, W, y, lse, -100, start, total, 1.0, dH,
+                                   dW, 0, ws, ws_bytes, None)
+
+
+def test_backward_shard_validation(lib):
+    p = flce.flce_plan(100, 64, 1000, "bf16")
+    assert _bwd_shard(lib, flce.Plan(), 0, 2000) == flce.FLCE_ERR_INVALID_ARG
+    assert _bwd_shard(lib, p, 1001, 2000) == flce.FLCE_ERR_INVALID_ARG
+    assert _bwd_shard(lib, p, -5, 2000) == flce.FLCE_ERR_INVALID_ARG
+    assert _bwd_shard(lib, p, 0, 2000, dW=None) == flce.FLCE_ERR_INVALID_ARG
+    assert _bwd_shard(lib, p, 0, 2000, dH=20) == flce.FLCE_ERR_UNSUPPORTED
+    assert _bwd_shard(lib, p, 1000, 2000, ws_bytes=p.bwd_ws_bytes - 1) == flce.FLCE_ERR_WORKSPACE
