@@ -241,6 +241,36 @@ def shard_leg(flce, wl, H, W, cfg, ws, stream, steps: int):
             "merge_avg_ms": round(merge["total_ms"] / max(1, merge["launches"]), 4)}
 
 
+def scoring_leg(flce, H, W, y, lse, stream, reps: int = 5):
+    """flce_token_logprobs on the step's inputs: K = 1 (the targets) and K = 8
+    tokens per position.  HBM-bound: algorithmic bytes = H once + K gathered
+    W rows per position + tokens, lse and outputs, against the 8 TB/s peak."""
+    import torch
+    T, d = H.shape
+    esz = H.element_size()
+    out = {}
+    for K in (1, 8):
+        tok = y.view(-1, 1) if K == 1 else torch.randint(0, W.shape[0], (T, K), device=W.device,
+                                                          generator=torch.Generator(W.device).manual_seed(5))
+        res = torch.empty((T, K), dtype=torch.float32, device=W.device)
+        flce.flce_token_logprobs(H, W, tok, lse, out=res, stream=stream)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            flce.flce_token_logprobs(H, W, tok, lse, out=res, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        nbytes = T * d * esz * (1 + K) + T * K * 12 + T * 4
+        gbs = nbytes / (ms / 1e3) / 1e9
+        out[f"K{K}"] = {"ms": round(ms, 4), "bytes": int(nbytes), "GB/s": round(gbs, 1),
+                        "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+        log(f"  token scoring K={K}: {ms:.3f} ms, {gbs:.0f} GB/s")
+    return out
+
+
 def copy_calibration(mib: int):
     """A plain copy of mib MiB (read mib, write mib), three times: the byte
     counters of a profiler run over it give the scale of FETCH_SIZE and
@@ -374,6 +404,7 @@ def main():
                 "avg_launch_ms": round(avg_ms, 4), "launches": dom["launches"]}
 
     shard = shard_leg(flce, wl, H, W, cfg, ws, stream, args.shard_steps) if args.shard_steps > 0 else None
+    scoring = scoring_leg(flce, H, W, y, lse, stream) if args.shard_steps > 0 else None
 
     cpu = None
     if args.cpu_rows > 0:
@@ -412,6 +443,7 @@ def main():
                     for k, v in kernels.items()},
         "kernel_ms_per_step": round(step_kernel_ms, 3),
         "shard_mode": shard,
+        "token_scoring": scoring,
         "plan": {"fwd_splits": plan.fwd_splits, "bwd_block": plan.bwd_block,
                  "bwd_slab": plan.bwd_slab, "n_blocks": plan.n_blocks, "n_slabs": plan.n_slabs},
     }

@@ -186,6 +186,25 @@ flce_status_t flce_backward_shard(const flce_plan_t* plan, const void* H, const 
                                   void* dH_partial, float* dW_shard, int accumulate_dW, void* ws,
                                   uint64_t ws_bytes, void* stream);
 
+/* flce_token_logprobs -- log-probabilities of given tokens.
+ *   out[t*K + k] = H[t] . W[tokens[t*K + k]] - lse[t]: the log-softmax of
+ *   the logits of the first page's section 3 at the named tokens, given the
+ *   lse that flce_forward (or flce_merge_shards) returned for the same H, W.
+ *   With lse == NULL, out holds the logits themselves.  Per-token log-probs
+ *   of the targets are -loss; this call scores any K tokens per position
+ *   (sampled tokens, candidates) with one gathered dot product each, no new
+ *   vocabulary sweep.
+ *   H [T x d], W [V x d] in dtype; tokens [T x K] int64; out [T x K] float.
+ *   Tokens outside [0, V) score NaN.  The dot product is fp32 (exact bf16
+ *   products) summed in a fixed order, so it may differ from the forward's
+ *   target logit by fp32 rounding.
+ * FLCE_ERR_INVALID_ARG for an unknown dtype, negative sizes or NULL buffers
+ * (T, K > 0), FLCE_ERR_UNSUPPORTED for d % 8 != 0, sizes beyond the plan's
+ * limits or misaligned H/W.  T == 0 or K == 0 launches nothing. */
+flce_status_t flce_token_logprobs(int64_t T, int64_t d, int64_t V, flce_dtype_t dtype,
+                                  const void* H, const void* W, const int64_t* tokens, int64_t K,
+                                  const float* lse, float* out, void* stream);
+
 /* ---- kernel timing (a profiling aid; off by default) --------------------
  * While enabled, every kernel launch made by flce_forward / flce_backward on
  * the calling process is bracketed by two hipEvents recorded on the caller's

@@ -23,7 +23,7 @@ FLCE_ERR_WORKSPACE = -3
 FLCE_ERR_HIP = -4
 
 EXPORTED = ["flce_plan", "flce_forward", "flce_backward", "flce_forward_shard",
-            "flce_merge_shards", "flce_backward_shard", "flce_timing_enable",
+            "flce_merge_shards", "flce_backward_shard", "flce_token_logprobs", "flce_timing_enable",
             "flce_timing_collect", "flce_status_string", "flce_last_error", "flce_version"]
 
 
@@ -88,6 +88,8 @@ def load(path: str = LIB_PATH):
     lib.flce_backward_shard.argtypes = [P, vp, vp, vp, vp, i64, i64, i64, f32, vp, vp,
                                         ctypes.c_int, vp, u64, vp]
     lib.flce_backward_shard.restype = ctypes.c_int
+    lib.flce_token_logprobs.argtypes = [i64, i64, i64, ctypes.c_int, vp, vp, vp, i64, vp, vp, vp]
+    lib.flce_token_logprobs.restype = ctypes.c_int
     lib.flce_timing_enable.argtypes = [ctypes.c_int]
     lib.flce_timing_enable.restype = ctypes.c_int
     lib.flce_timing_collect.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int,
@@ -335,3 +337,27 @@ def flce_backward_shard(plan: Plan, H, W_shard, y, lse, vocab_start: int, vocab_
                                       _ptr(dW_shard), 1 if accumulate_dW else 0, _ptr(ws),
                                       int(ws.numel() * ws.element_size()), _stream(stream)))
     return dH_partial, dW_shard
+
+
+def flce_token_logprobs(H, W, tokens, lse=None, out=None, stream=None):
+    """flce_token_logprobs(): out [T, K] = H[t] . W[tokens[t, k]] - lse[t].
+
+    tokens: int64 [T, K] (or [T] for K = 1); lse None gives the logits."""
+    import torch
+    if H.dim() != 2 or W.dim() != 2 or H.shape[1] != W.shape[1] or H.dtype != W.dtype:
+        raise ValueError("H [T, d] and W [V, d] of one dtype")
+    T, d = H.shape
+    V = W.shape[0]
+    tok = tokens if tokens.dim() == 2 else tokens.view(-1, 1)
+    K = tok.shape[1]
+    _check_tensor("H", H, (T, d), H.dtype)
+    _check_tensor("W", W, (V, d), H.dtype)
+    _check_tensor("tokens", tok, (T, K), torch.int64)
+    _check_tensor("lse", lse, (T,), torch.float32)
+    if out is None:
+        out = torch.empty((T, K), dtype=torch.float32, device=W.device)
+    _check_tensor("out", out, (T, K), torch.float32)
+    _check(load().flce_token_logprobs(int(T), int(d), int(V), _dtype_code(H.dtype), _ptr(H),
+                                      _ptr(W), _ptr(tok), int(K), _ptr(lse), _ptr(out),
+                                      _stream(stream)))
+    return out if tokens.dim() == 2 else out.view(-1)

@@ -56,10 +56,12 @@ flce_status_t hip_fail(hipError_t e, const char* what) {
 
 // ------------------------------------------------------------ kernel timing
 enum KernelId {
-  K_FWD_SWEEP, K_FWD_MERGE, K_LOSS_SUM, K_BWD_DZ, K_BWD_DH, K_BWD_DW, K_FILL, K_SHARD_MERGE, K_COUNT
+  K_FWD_SWEEP, K_FWD_MERGE, K_LOSS_SUM, K_BWD_DZ, K_BWD_DH, K_BWD_DW, K_FILL, K_SHARD_MERGE,
+  K_TOKEN_LOGIT, K_COUNT
 };
-const char* const kKernelNames[K_COUNT] = {"fwd_sweep", "fwd_merge", "loss_sum",  "bwd_dz",
-                                           "bwd_dh",    "bwd_dw",    "fill_zero", "shard_merge"};
+const char* const kKernelNames[K_COUNT] = {"fwd_sweep", "fwd_merge", "loss_sum",    "bwd_dz",
+                                           "bwd_dh",    "bwd_dw",    "fill_zero",   "shard_merge",
+                                           "token_logit"};
 
 struct TimingRec {
   int kid;
@@ -587,6 +589,43 @@ flce_status_t flce_backward_shard(const flce_plan_t* plan, const void* H, const 
   const flce::Targets tg{y, ignore_index, vocab_start, vocab_total};
   return backward_impl(plan, H, W_shard, tg, lse, grad_scale, dH_partial, dW_shard, accumulate_dW,
                        ws, ws_bytes, stream);
+}
+
+flce_status_t flce_token_logprobs(int64_t T, int64_t d, int64_t V, flce_dtype_t dtype,
+                                  const void* H, const void* W, const int64_t* tokens, int64_t K,
+                                  const float* lse, float* out, void* stream) {
+  if (dtype != FLCE_F32 && dtype != FLCE_BF16)
+    return fail(FLCE_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (T < 0 || V < 1 || d < 1 || K < 0)
+    return fail(FLCE_ERR_INVALID_ARG, "sizes T=%lld d=%lld V=%lld K=%lld out of range", (long long)T,
+                (long long)d, (long long)V, (long long)K);
+  if (d % 8 != 0) return fail(FLCE_ERR_UNSUPPORTED, "d = %lld is not a multiple of 8", (long long)d);
+  if (T >= ((int64_t)1 << 31) || V >= ((int64_t)1 << 31) || d > 65536 || K >= ((int64_t)1 << 31) ||
+      (K > 0 && T > (((int64_t)1 << 62) / K)))
+    return fail(FLCE_ERR_UNSUPPORTED, "sizes beyond the limits");
+  if (T == 0 || K == 0) return ok();
+  if (!H || !W || !tokens || !out)
+    return fail(FLCE_ERR_INVALID_ARG, "H, W, tokens and out must be non-NULL");
+  if (misaligned(H) || misaligned(W))
+    return fail(FLCE_ERR_UNSUPPORTED, "H and W must be 16-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  flce::TokenArgs a;
+  a.H = H;
+  a.W = W;
+  a.tokens = tokens;
+  a.lse = lse;
+  a.T = T;
+  a.d = (int)d;
+  a.V = (int)V;
+  a.K = (int)K;
+  a.out = out;
+  const double esz = dtype == FLCE_BF16 ? 2.0 : 4.0;
+  Timed tm(s, K_TOKEN_LOGIT, 2.0 * T * K * d,
+           (double)T * d * esz * (1.0 + K) + T * K * 12.0 + (lse ? T * 4.0 : 0.0));
+  const hipError_t e = flce::launch_token_logit(a, dtype == FLCE_BF16, s);
+  tm.done();
+  if (e != hipSuccess) return hip_fail(e, "token logit launch");
+  return ok();
 }
 
 }  // extern "C"

@@ -654,6 +654,54 @@ __global__ void __launch_bounds__(256) fill_zero_kernel(float* p, int64_t n) {
   }
 }
 
+// ============================================================= token scoring
+// One wave per token position: the lanes stride over 16-byte chunks of H[t]
+// and of the token's W row (both rows read contiguously, 1 KB per wave
+// instruction), multiply in fp32 (exact for bf16 inputs), and a fixed xor
+// tree sums the wave.  Tokens outside [0, V) score NaN.
+__device__ __forceinline__ float dot16(const u32x4_t& h, const u32x4_t& w, float acc, __bf16*) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc = fmaf(__builtin_bit_cast(float, h[q] << 16), __builtin_bit_cast(float, w[q] << 16), acc);
+    acc = fmaf(__builtin_bit_cast(float, h[q] & 0xffff0000u),
+               __builtin_bit_cast(float, w[q] & 0xffff0000u), acc);
+  }
+  return acc;
+}
+__device__ __forceinline__ float dot16(const u32x4_t& h, const u32x4_t& w, float acc, float*) {
+  // whole-vector casts: a bit_cast of one element of a vector lvalue reads
+  // element 0 with this compiler
+  const f32x4_t hf = __builtin_bit_cast(f32x4_t, h), wf = __builtin_bit_cast(f32x4_t, w);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc = fmaf(hf[q], wf[q], acc);
+  return acc;
+}
+
+template <typename E>
+__global__ void __launch_bounds__(256) token_logit_kernel(TokenArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  if (t >= a.T) return;
+  constexpr int CW = 16 / (int)sizeof(E);
+  const int nc = a.d / CW;
+  const char* h = reinterpret_cast<const char*>(a.H) + t * a.d * (int64_t)sizeof(E);
+  const float lse = a.lse ? a.lse[t] : 0.f;
+  for (int k = 0; k < a.K; ++k) {
+    const int64_t v = a.tokens[t * a.K + k];
+    const bool ok = v >= 0 && v < a.V;
+    float acc = 0.f;
+    if (ok) {
+      const char* w = reinterpret_cast<const char*>(a.W) + v * a.d * (int64_t)sizeof(E);
+      for (int c = lane; c < nc; c += 64)
+        acc = dot16(*reinterpret_cast<const u32x4_t*>(h + (int64_t)c * 16),
+                    *reinterpret_cast<const u32x4_t*>(w + (int64_t)c * 16), acc, (E*)nullptr);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+    if (lane == 0) a.out[t * a.K + k] = ok ? acc - lse : __builtin_nanf("");
+  }
+}
+
 // ================================================================== launchers
 template <typename K, typename Args>
 static hipError_t launch(K kernel, int grid, int threads, int lds, hipStream_t s, const Args& args) {
@@ -688,6 +736,12 @@ hipError_t launch_fwd_merge(const MergeArgs& a, hipStream_t s) {
 hipError_t launch_loss_sum(const float* loss, int64_t T, float scale, float* out, hipStream_t s) {
   hipLaunchKernelGGL(loss_sum_kernel, dim3(1), dim3(1024), 0, s, loss, T, scale, out);
   return hipGetLastError();
+}
+
+hipError_t launch_token_logit(const TokenArgs& a, bool bf16, hipStream_t s) {
+  const int grid = (int)((a.T + 3) / 4);
+  if (bf16) return launch(token_logit_kernel<__bf16>, grid, 256, 0, s, a);
+  return launch(token_logit_kernel<float>, grid, 256, 0, s, a);
 }
 
 hipError_t launch_shard_merge(const ShardMergeArgs& a, hipStream_t s) {

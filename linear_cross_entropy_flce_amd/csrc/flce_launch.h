@@ -113,7 +113,20 @@ hipError_t launch_loss_sum(const float* loss, int64_t T, float scale, float* out
 hipError_t launch_bwd_dz(const DzArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_dh(const DhArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_dw(const DwArgs& a, bool bf16, hipStream_t s);
+// Scoring of given tokens: out[t * K + k] = H[t] . W[tokens[t * K + k]] - lse[t]
+// (lse NULL: the logit itself).
+struct TokenArgs {
+  const void* H;
+  const void* W;
+  const int64_t* tokens;
+  const float* lse;
+  int64_t T;
+  int d, V, K;
+  float* out;
+};
+
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+hipError_t launch_token_logit(const TokenArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_shard_merge(const ShardMergeArgs& a, hipStream_t s);
 
 }  // namespace flce

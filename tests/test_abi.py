@@ -215,3 +215,23 @@ def test_backward_shard_validation(lib):
     assert _bwd_shard(lib, p, 0, 2000, dW=None) == flce.FLCE_ERR_INVALID_ARG
     assert _bwd_shard(lib, p, 0, 2000, dH=20) == flce.FLCE_ERR_UNSUPPORTED
     assert _bwd_shard(lib, p, 1000, 2000, ws_bytes=p.bwd_ws_bytes - 1) == flce.FLCE_ERR_WORKSPACE
+
+
+def _tok(lib, T=10, d=64, V=100, dt=flce.FLCE_BF16, H=16, W=16, tok=16, K=2, lse=None, out=16):
+    return lib.flce_token_logprobs(T, d, V, dt, H, W, tok, K, lse, out, None)
+
+
+def test_token_logprobs_validation(lib):
+    assert _tok(lib, dt=7) == flce.FLCE_ERR_INVALID_ARG
+    assert _tok(lib, T=-1) == flce.FLCE_ERR_INVALID_ARG
+    assert _tok(lib, V=0) == flce.FLCE_ERR_INVALID_ARG
+    assert _tok(lib, K=-1) == flce.FLCE_ERR_INVALID_ARG
+    assert _tok(lib, d=60) == flce.FLCE_ERR_UNSUPPORTED
+    assert _tok(lib, d=65544) == flce.FLCE_ERR_UNSUPPORTED
+    assert _tok(lib, V=1 << 31) == flce.FLCE_ERR_UNSUPPORTED
+    assert _tok(lib, out=None) == flce.FLCE_ERR_INVALID_ARG
+    assert _tok(lib, tok=None) == flce.FLCE_ERR_INVALID_ARG
+    assert _tok(lib, W=40) == flce.FLCE_ERR_UNSUPPORTED
+    # nothing to score: no launch, no buffers needed
+    assert _tok(lib, T=0, H=None, W=None, tok=None, out=None) == flce.FLCE_OK
+    assert _tok(lib, K=0, H=None, W=None, tok=None, out=None) == flce.FLCE_OK
