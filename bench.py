@@ -241,6 +241,40 @@ def shard_leg(flce, wl, H, W, cfg, ws, stream, steps: int):
             "merge_avg_ms": round(merge["total_ms"] / max(1, merge["launches"]), 4)}
 
 
+def fused_leg(flce, wl, plan, H, W, y, ws, stream, steps: int):
+    """The same step as one flce_forward_backward call with the mean over
+    non-ignored tokens (count and gradient scale on the device) and the bf16
+    copy of dW."""
+    import torch
+    T, d, V = plan.T, plan.d, plan.V
+    dev = W.device
+    loss = torch.empty(T, dtype=torch.float32, device=dev)
+    lse = torch.empty(T, dtype=torch.float32, device=dev)
+    red = torch.empty(1, dtype=torch.float32, device=dev)
+    dH = torch.empty((T, d), dtype=H.dtype, device=dev)
+    dW = torch.empty((V, d), dtype=torch.float32, device=dev)
+    dWb = torch.empty((V, d), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        flce.flce_forward_backward(plan, H, W, y, wl.IGNORE_INDEX, "mean_valid", 1.0, loss=loss,
+                                   lse=lse, loss_reduced=red, dH=dH, dW=dW, dW_bf16=dWb, ws=ws,
+                                   stream=stream)
+
+    step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    log(f"  fused call (mean over valid tokens, bf16 dW copy): {ms:.2f} ms/step")
+    return {"reduction": "mean_valid", "dW_bf16": True, "steps": steps, "ms_per_step": round(ms, 3),
+            "tflops": round(8.0 * T * d * V / ms / 1e9, 2)}
+
+
 def scoring_leg(flce, H, W, y, lse, stream, reps: int = 5):
     """flce_token_logprobs on the step's inputs: K = 1 (the targets) and K = 8
     tokens per position.  HBM-bound: algorithmic bytes = H once + K gathered
@@ -294,8 +328,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3, help="workload index (default 3)")
     ap.add_argument("--shard-steps", type=int, default=3,
-                    help="steps of the vocab-shard leg: W as rank 1 of 2 of a vocabulary of 2V "
-                         "ids (0 skips it)")
+                    help="steps of each extra leg (vocab shard: W as rank 1 of 2 of a 2V-id "
+                         "vocabulary; fused call; token scoring); 0 skips them")
     ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="rows of the CPU-oracle sample (0 skips it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
@@ -405,6 +439,7 @@ def main():
 
     shard = shard_leg(flce, wl, H, W, cfg, ws, stream, args.shard_steps) if args.shard_steps > 0 else None
     scoring = scoring_leg(flce, H, W, y, lse, stream) if args.shard_steps > 0 else None
+    fused = fused_leg(flce, wl, plan, H, W, y, ws, stream, args.shard_steps) if args.shard_steps > 0 else None
 
     cpu = None
     if args.cpu_rows > 0:
@@ -444,6 +479,7 @@ def main():
         "kernel_ms_per_step": round(step_kernel_ms, 3),
         "shard_mode": shard,
         "token_scoring": scoring,
+        "fused_call": fused,
         "plan": {"fwd_splits": plan.fwd_splits, "bwd_block": plan.bwd_block,
                  "bwd_slab": plan.bwd_slab, "n_blocks": plan.n_blocks, "n_slabs": plan.n_slabs},
     }

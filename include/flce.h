@@ -76,7 +76,8 @@ typedef struct flce_plan {
   uint64_t dz_ws_bytes;    /* the [bwd_block x bwd_slab] dZ tile buffer */
   uint64_t dh_acc_bytes;   /* fp32 dH accumulator, 0 when there is one slab */
   uint64_t bwd_ws_bytes;   /* dz_ws_bytes + dh_acc_bytes */
-  uint64_t ws_bytes;       /* max(fwd_ws_bytes, bwd_ws_bytes) */
+  uint64_t ws_bytes;       /* max(fwd_ws_bytes, bwd_ws_bytes) + 256: enough for every call,
+                              flce_forward_backward's device scalars included */
   uint64_t vocab_ws_cap;   /* the cap the planner honoured */
   /* context: bytes of one materialised [T x V] logits copy in the dtype */
   uint64_t naive_logits_bytes;
@@ -126,6 +127,33 @@ flce_status_t flce_backward(const flce_plan_t* plan, const void* H, const void* 
                             const int64_t* y, const float* lse, int64_t ignore_index,
                             float grad_scale, void* dH, float* dW, int accumulate_dW, void* ws,
                             uint64_t ws_bytes, void* stream);
+
+/* How flce_forward_backward reduces the per-token losses. */
+typedef enum {
+  FLCE_REDUCE_SUM = 0,        /* loss_reduced = scale * sum(loss), g = scale */
+  FLCE_REDUCE_MEAN_VALID = 1  /* divided by the number of tokens with y != ignore_index,
+                                 counted on the device (0 tokens: loss_reduced = 0, g = 0) */
+} flce_reduction_t;
+
+/* flce_forward_backward -- forward, reduction and backward in one call, for
+ * training steps where the gradient scale follows from the reduction: the
+ * mean over non-ignored tokens needs their count, which is taken on the GPU
+ * and passed to the backward there, with no host round trip.
+ *   Arguments as flce_forward and flce_backward; grad scale g as above.
+ *   dW [V x d] float: overwritten, or accumulated into when accumulate_dW
+ *       != 0 (the fp32 main gradient across micro-batches).
+ *   dW_bf16 : NULL, or [V x d] bf16 that receives dW rounded to nearest
+ *       even after the call's accumulation.
+ *   ws, ws_bytes : at least plan->ws_bytes.
+ * Errors as flce_forward / flce_backward, and FLCE_ERR_INVALID_ARG for an
+ * unknown reduction.  Outputs equal flce_forward then flce_backward with the
+ * same g, bit for bit. */
+flce_status_t flce_forward_backward(const flce_plan_t* plan, const void* H, const void* W,
+                                    const int64_t* y, int64_t ignore_index,
+                                    flce_reduction_t reduction, float scale, float* loss,
+                                    float* lse, float* loss_reduced, void* dH, float* dW,
+                                    int accumulate_dW, void* dW_bf16, void* ws, uint64_t ws_bytes,
+                                    void* stream);
 
 /* ---- vocab-parallel shard mode ------------------------------------------
  * The Megatron-Lite / bumblebee write-up (section 2.3, step 1) runs this loss

@@ -5,14 +5,16 @@ through the C-ABI declared in include/flce.h; this package only marshals
 arguments (torch supplies device memory and the stream).
 """
 from ._lib import (EXPORTED, FLCE_BF16, FLCE_ERR_HIP, FLCE_ERR_INVALID_ARG, FLCE_ERR_UNSUPPORTED,
-                   FLCE_ERR_WORKSPACE, FLCE_F32, FLCE_OK, FlceError, KernelTime, Plan, flce_backward,
-                   flce_backward_shard, flce_forward, flce_forward_shard, flce_merge_shards,
+                   FLCE_ERR_WORKSPACE, FLCE_F32, FLCE_OK, FLCE_REDUCE_MEAN_VALID, FLCE_REDUCE_SUM,
+                   FlceError, KernelTime, Plan, flce_backward, flce_backward_shard, flce_forward,
+                   flce_forward_backward, flce_forward_shard, flce_merge_shards,
                    flce_plan, flce_plan_status, flce_timing_collect, flce_timing_enable,
                    flce_token_logprobs, last_error, load, version, workspace)
 
 __all__ = ["EXPORTED", "FLCE_BF16", "FLCE_ERR_HIP", "FLCE_ERR_INVALID_ARG", "FLCE_ERR_UNSUPPORTED",
-           "FLCE_ERR_WORKSPACE", "FLCE_F32", "FLCE_OK", "FlceError", "KernelTime", "Plan",
-           "flce_backward", "flce_backward_shard", "flce_forward", "flce_forward_shard",
+           "FLCE_ERR_WORKSPACE", "FLCE_F32", "FLCE_OK", "FLCE_REDUCE_MEAN_VALID", "FLCE_REDUCE_SUM",
+           "FlceError", "KernelTime", "Plan", "flce_backward", "flce_backward_shard",
+           "flce_forward", "flce_forward_backward", "flce_forward_shard",
            "flce_merge_shards", "flce_plan", "flce_plan_status", "flce_timing_collect",
            "flce_timing_enable", "flce_token_logprobs", "last_error", "load", "version",
            "workspace"]

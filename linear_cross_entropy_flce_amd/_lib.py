@@ -21,8 +21,11 @@ FLCE_ERR_INVALID_ARG = -1
 FLCE_ERR_UNSUPPORTED = -2
 FLCE_ERR_WORKSPACE = -3
 FLCE_ERR_HIP = -4
+FLCE_REDUCE_SUM = 0
+FLCE_REDUCE_MEAN_VALID = 1
 
-EXPORTED = ["flce_plan", "flce_forward", "flce_backward", "flce_forward_shard",
+EXPORTED = ["flce_plan", "flce_forward", "flce_backward", "flce_forward_backward",
+            "flce_forward_shard",
             "flce_merge_shards", "flce_backward_shard", "flce_token_logprobs", "flce_timing_enable",
             "flce_timing_collect", "flce_status_string", "flce_last_error", "flce_version"]
 
@@ -80,6 +83,9 @@ def load(path: str = LIB_PATH):
     lib.flce_forward.restype = ctypes.c_int
     lib.flce_backward.argtypes = [P, vp, vp, vp, vp, i64, f32, vp, vp, ctypes.c_int, vp, u64, vp]
     lib.flce_backward.restype = ctypes.c_int
+    lib.flce_forward_backward.argtypes = [P, vp, vp, vp, i64, ctypes.c_int, f32, vp, vp, vp, vp,
+                                          vp, ctypes.c_int, vp, vp, u64, vp]
+    lib.flce_forward_backward.restype = ctypes.c_int
     lib.flce_forward_shard.argtypes = [P, vp, vp, vp, i64, i64, i64, vp, vp, vp, u64, vp]
     lib.flce_forward_shard.restype = ctypes.c_int
     lib.flce_merge_shards.argtypes = [i64, ctypes.c_int32, vp, vp, vp, i64, i64, f32, vp, vp, vp,
@@ -361,3 +367,53 @@ def flce_token_logprobs(H, W, tokens, lse=None, out=None, stream=None):
                                       _ptr(W), _ptr(tok), int(K), _ptr(lse), _ptr(out),
                                       _stream(stream)))
     return out if tokens.dim() == 2 else out.view(-1)
+
+
+_REDUCTIONS = {"sum": FLCE_REDUCE_SUM, "mean_valid": FLCE_REDUCE_MEAN_VALID,
+               FLCE_REDUCE_SUM: FLCE_REDUCE_SUM, FLCE_REDUCE_MEAN_VALID: FLCE_REDUCE_MEAN_VALID}
+
+
+def flce_forward_backward(plan: Plan, H, W, y, ignore_index: int = -100, reduction="sum",
+                          scale: float = 1.0, loss=None, lse=None, loss_reduced=None, dH=None,
+                          dW=None, accumulate_dW: bool = False, dW_bf16=None, ws=None,
+                          stream=None):
+    """flce_forward_backward(): returns dict(loss, lse, loss_reduced, dH, dW, dW_bf16).
+
+    reduction: "sum" (g = scale) or "mean_valid" (g = scale / #non-ignored
+    tokens, counted on the device)."""
+    import torch
+    T, d, V = plan.T, plan.d, plan.V
+    dev = W.device
+    et = _elem_dtype(plan)
+    if reduction not in _REDUCTIONS:
+        raise ValueError(f"unknown reduction {reduction!r}")
+    _check_tensor("H", H, (T, d), et)
+    _check_tensor("W", W, (V, d), et)
+    _check_tensor("y", y, (T,), torch.int64)
+    if loss is None:
+        loss = torch.empty(T, dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(T, dtype=torch.float32, device=dev)
+    if loss_reduced is None:
+        loss_reduced = torch.empty(1, dtype=torch.float32, device=dev)
+    if dH is None:
+        dH = torch.empty((T, d), dtype=et, device=dev)
+    if dW is None:
+        if accumulate_dW:
+            raise ValueError("accumulate_dW needs an existing dW")
+        dW = torch.empty((V, d), dtype=torch.float32, device=dev)
+    _check_tensor("loss", loss, (T,), torch.float32)
+    _check_tensor("lse", lse, (T,), torch.float32)
+    _check_tensor("loss_reduced", loss_reduced, (1,), torch.float32)
+    _check_tensor("dH", dH, (T, d), et)
+    _check_tensor("dW", dW, (V, d), torch.float32)
+    _check_tensor("dW_bf16", dW_bf16, (V, d), torch.bfloat16)
+    if ws is None:
+        ws = workspace(plan, dev)
+    _check(load().flce_forward_backward(ctypes.byref(plan), _ptr(H), _ptr(W), _ptr(y),
+                                        int(ignore_index), _REDUCTIONS[reduction], float(scale),
+                                        _ptr(loss), _ptr(lse), _ptr(loss_reduced), _ptr(dH),
+                                        _ptr(dW), 1 if accumulate_dW else 0, _ptr(dW_bf16),
+                                        _ptr(ws), int(ws.numel() * ws.element_size()),
+                                        _stream(stream)))
+    return dict(loss=loss, lse=lse, loss_reduced=loss_reduced, dH=dH, dW=dW, dW_bf16=dW_bf16)

@@ -23,6 +23,9 @@ constexpr uint64_t kMaxCap = 0x7fff0000ull;
 constexpr int64_t kMaxBlock = 8192;
 constexpr int kTargetWorkgroups = 256;  // one per compute unit
 constexpr int64_t kComputeUnits = 256;  // MI355X
+// device scalars of flce_forward_backward (the gradient scale), after the
+// larger of the forward and backward workspaces
+constexpr uint64_t kScalarBytes = 256;
 
 thread_local char g_err[512] = "";
 
@@ -57,11 +60,11 @@ flce_status_t hip_fail(hipError_t e, const char* what) {
 // ------------------------------------------------------------ kernel timing
 enum KernelId {
   K_FWD_SWEEP, K_FWD_MERGE, K_LOSS_SUM, K_BWD_DZ, K_BWD_DH, K_BWD_DW, K_FILL, K_SHARD_MERGE,
-  K_TOKEN_LOGIT, K_COUNT
+  K_TOKEN_LOGIT, K_CAST, K_COUNT
 };
 const char* const kKernelNames[K_COUNT] = {"fwd_sweep", "fwd_merge", "loss_sum",    "bwd_dz",
                                            "bwd_dh",    "bwd_dw",    "fill_zero",   "shard_merge",
-                                           "token_logit"};
+                                           "token_logit", "cast_bf16"};
 
 struct TimingRec {
   int kid;
@@ -153,6 +156,11 @@ double backward_cost(int64_t T, int64_t d, int64_t V, int64_t B, int64_t Vs,
 
 namespace {
 
+hipError_t launch_loss_sum(const float* loss, int64_t T, float scale, float* out, hipStream_t s) {
+  flce::ReduceArgs r{loss, nullptr, 0, T, scale, 0, out, nullptr};
+  return flce::launch_loss_reduce(r, s);
+}
+
 flce_status_t check_shard(const flce_plan_t& p, int64_t vocab_start, int64_t vocab_total) {
   if (vocab_total < 1 || vocab_total >= ((int64_t)1 << 31))
     return fail(FLCE_ERR_INVALID_ARG, "vocab_total = %lld out of range", (long long)vocab_total);
@@ -187,7 +195,7 @@ flce_status_t forward_impl(const flce_plan_t* plan, const void* H, const void* W
   if (p.T == 0) {
     if (loss_reduced) {
       Timed tm(s, K_LOSS_SUM, 0, 4);
-      e = flce::launch_loss_sum(loss, 0, scale, loss_reduced, s);
+      e = launch_loss_sum(loss, 0, scale, loss_reduced, s);
       tm.done();
       if (e != hipSuccess) return hip_fail(e, "loss_sum launch");
     }
@@ -236,7 +244,7 @@ flce_status_t forward_impl(const flce_plan_t* plan, const void* H, const void* W
   if (e != hipSuccess) return hip_fail(e, "forward merge launch");
   if (loss_reduced) {
     Timed tm(s, K_LOSS_SUM, 0, p.T * 4.0 + 4);
-    e = flce::launch_loss_sum(loss, p.T, scale, loss_reduced, s);
+    e = launch_loss_sum(loss, p.T, scale, loss_reduced, s);
     tm.done();
     if (e != hipSuccess) return hip_fail(e, "loss_sum launch");
   }
@@ -246,9 +254,9 @@ flce_status_t forward_impl(const flce_plan_t* plan, const void* H, const void* W
 // The backward for one vocab shard (the whole vocabulary when tg.start = 0
 // and tg.total = V); lse is over the whole vocabulary.
 flce_status_t backward_impl(const flce_plan_t* plan, const void* H, const void* W,
-                            const flce::Targets& tg, const float* lse, float grad_scale, void* dH,
-                            float* dW, int accumulate_dW, void* ws, uint64_t ws_bytes,
-                            void* stream) {
+                            const flce::Targets& tg, const float* lse, float grad_scale,
+                            const float* g_dev, void* dH, float* dW, int accumulate_dW, void* ws,
+                            uint64_t ws_bytes, void* stream) {
   flce_status_t st = check_plan(plan);
   if (st != FLCE_OK) return st;
   const flce_plan_t& p = *plan;
@@ -300,6 +308,7 @@ flce_status_t backward_impl(const flce_plan_t* plan, const void* H, const void* 
       z.ldz = p.bwd_slab;
       z.ldz_cols = (int64_t)z.n_vtiles * ti.logit_bm;
       z.grad_scale = grad_scale;
+      z.g_dev = g_dev;
       z.dz = dz;
       const double esz = (double)p.elem_bytes;
       const double tc = t_count, vc = v_count, dd = (double)p.d;
@@ -497,7 +506,7 @@ flce_status_t flce_plan(int64_t T, int64_t d, int64_t V, flce_dtype_t dtype, uin
   p.dz_ws_bytes = (uint64_t)(best_B * best_Vs * esz);
   p.dh_acc_bytes = best_slabs > 1 ? (uint64_t)(best_B * d * 4) : 0;
   p.bwd_ws_bytes = p.dz_ws_bytes + p.dh_acc_bytes;
-  p.ws_bytes = p.fwd_ws_bytes > p.bwd_ws_bytes ? p.fwd_ws_bytes : p.bwd_ws_bytes;
+  p.ws_bytes = (p.fwd_ws_bytes > p.bwd_ws_bytes ? p.fwd_ws_bytes : p.bwd_ws_bytes) + kScalarBytes;
   p.vocab_ws_cap = cap;
   p.naive_logits_bytes = (uint64_t)T * (uint64_t)V * (uint64_t)esz;
   p.magic = kPlanMagic;
@@ -522,8 +531,59 @@ flce_status_t flce_backward(const flce_plan_t* plan, const void* H, const void* 
   const flce_status_t st = check_plan(plan);
   if (st != FLCE_OK) return st;
   const flce::Targets tg{y, ignore_index, 0, plan->V};
-  return backward_impl(plan, H, W, tg, lse, grad_scale, dH, dW, accumulate_dW, ws, ws_bytes,
-                       stream);
+  return backward_impl(plan, H, W, tg, lse, grad_scale, nullptr, dH, dW, accumulate_dW, ws,
+                       ws_bytes, stream);
+}
+
+flce_status_t flce_forward_backward(const flce_plan_t* plan, const void* H, const void* W,
+                                    const int64_t* y, int64_t ignore_index,
+                                    flce_reduction_t reduction, float scale, float* loss,
+                                    float* lse, float* loss_reduced, void* dH, float* dW,
+                                    int accumulate_dW, void* dW_bf16, void* ws, uint64_t ws_bytes,
+                                    void* stream) {
+  flce_status_t st = check_plan(plan);
+  if (st != FLCE_OK) return st;
+  const flce_plan_t& p = *plan;
+  if (reduction != FLCE_REDUCE_SUM && reduction != FLCE_REDUCE_MEAN_VALID)
+    return fail(FLCE_ERR_INVALID_ARG, "unknown reduction %d", (int)reduction);
+  if (!W || !dW) return fail(FLCE_ERR_INVALID_ARG, "W and dW must be non-NULL");
+  if (p.T > 0 && (!H || !y || !loss || !lse || !dH || !ws))
+    return fail(FLCE_ERR_INVALID_ARG, "H, y, loss, lse, dH and ws must be non-NULL when T > 0");
+  if (misaligned(H) || misaligned(W) || misaligned(dH) || misaligned(dW) || misaligned(ws) ||
+      misaligned(dW_bf16))
+    return fail(FLCE_ERR_UNSUPPORTED, "H, W, dH, dW, dW_bf16 and ws must be 16-byte aligned");
+  if (p.T > 0 && ws_bytes < p.ws_bytes)
+    return fail(FLCE_ERR_WORKSPACE, "forward_backward needs %llu workspace bytes, got %llu",
+                (unsigned long long)p.ws_bytes, (unsigned long long)ws_bytes);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  const flce::Targets tg{y, ignore_index, 0, p.V};
+  float* g_dev = nullptr;
+  if (p.T > 0) {
+    st = forward_impl(plan, H, W, tg, scale, loss, lse, nullptr, nullptr, false, ws, ws_bytes,
+                      stream);
+    if (st != FLCE_OK) return st;
+    g_dev = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + (p.ws_bytes - kScalarBytes));
+    flce::ReduceArgs r{loss, y, ignore_index, p.T, scale,
+                       reduction == FLCE_REDUCE_MEAN_VALID ? 1 : 0, loss_reduced, g_dev};
+    Timed tm(s, K_LOSS_SUM, 0, p.T * (reduction == FLCE_REDUCE_MEAN_VALID ? 12.0 : 4.0) + 8);
+    e = flce::launch_loss_reduce(r, s);
+    tm.done();
+    if (e != hipSuccess) return hip_fail(e, "loss reduce launch");
+  } else if (loss_reduced) {
+    e = launch_loss_sum(loss, 0, scale, loss_reduced, s);
+    if (e != hipSuccess) return hip_fail(e, "loss_sum launch");
+  }
+  st = backward_impl(plan, H, W, tg, lse, scale, g_dev, dH, dW, accumulate_dW, ws, ws_bytes,
+                     stream);
+  if (st != FLCE_OK) return st;
+  if (dW_bf16) {
+    Timed tm(s, K_CAST, 0, p.V * p.d * 6.0);
+    e = flce::launch_cast_bf16(dW, dW_bf16, p.V * p.d, s);
+    tm.done();
+    if (e != hipSuccess) return hip_fail(e, "dW cast launch");
+  }
+  return ok();
 }
 
 flce_status_t flce_forward_shard(const flce_plan_t* plan, const void* H, const void* W_shard,
@@ -570,7 +630,7 @@ flce_status_t flce_merge_shards(int64_t T, int32_t n_shards, const float* lse_sh
   }
   if (loss_reduced) {
     Timed tm(s, K_LOSS_SUM, 0, T * 4.0 + 4);
-    e = flce::launch_loss_sum(loss, T, scale, loss_reduced, s);
+    e = launch_loss_sum(loss, T, scale, loss_reduced, s);
     tm.done();
     if (e != hipSuccess) return hip_fail(e, "loss_sum launch");
   }
@@ -587,8 +647,8 @@ flce_status_t flce_backward_shard(const flce_plan_t* plan, const void* H, const 
   st = check_shard(*plan, vocab_start, vocab_total);
   if (st != FLCE_OK) return st;
   const flce::Targets tg{y, ignore_index, vocab_start, vocab_total};
-  return backward_impl(plan, H, W_shard, tg, lse, grad_scale, dH_partial, dW_shard, accumulate_dW,
-                       ws, ws_bytes, stream);
+  return backward_impl(plan, H, W_shard, tg, lse, grad_scale, nullptr, dH_partial, dW_shard,
+                       accumulate_dW, ws, ws_bytes, stream);
 }
 
 flce_status_t flce_token_logprobs(int64_t T, int64_t d, int64_t V, flce_dtype_t dtype,

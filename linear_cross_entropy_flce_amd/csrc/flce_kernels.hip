@@ -13,7 +13,7 @@
 //               vocab range, target logit captured from the fp32 accumulator;
 //               writes per-split (max, sum) partials and z_target.
 //   fwd_merge   merges the splits in ascending order: lse, loss.
-//   loss_sum    fixed-order double-precision sum for the reduced loss.
+//   loss_reduce fixed-order double-precision sum (and count) for the reduced loss.
 //   bwd_dz      recomputed logits tile -> dZ = g * (exp(z - lse) - onehot),
 //               stored (bf16 or fp32) to the [block x slab] workspace.
 //   bwd_dh      dH_block (+)= dZ W_slab   (fp32 accumulate, cast at the end).
@@ -347,20 +347,52 @@ __global__ void __launch_bounds__(256) shard_merge_kernel(ShardMergeArgs a) {
   a.loss[t] = loss;
 }
 
-// Fixed-order reduction: thread i sums loss[i], loss[i + 1024], ... in double,
-// then a tree over the 1024 threads.  One workgroup; deterministic.
-__global__ void __launch_bounds__(1024) loss_sum_kernel(const float* loss, int64_t T, float scale,
-                                                        float* out) {
+// Fixed-order reduction: thread i sums loss[i], loss[i + 1024], ... in double
+// (and, for a mean over the non-ignored tokens, counts them), then a tree over
+// the 1024 threads.  One workgroup; deterministic.  Writes the reduced loss
+// scale * sum (/ count) and the gradient scale of that reduction,
+// scale (/ count); a mean over no tokens is 0 with gradient scale 0.
+__global__ void __launch_bounds__(1024) loss_reduce_kernel(ReduceArgs a) {
   __shared__ double buf[1024];
+  __shared__ int64_t cnt[1024];
   double s = 0.0;
-  for (int64_t i = threadIdx.x; i < T; i += 1024) s += (double)loss[i];
+  int64_t c = 0;
+  for (int64_t i = threadIdx.x; i < a.T; i += 1024) {
+    s += (double)a.loss[i];
+    if (a.mean_valid) c += a.y[i] != a.ignore_index ? 1 : 0;
+  }
   buf[threadIdx.x] = s;
+  cnt[threadIdx.x] = c;
   __syncthreads();
   for (int w = 512; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w) buf[threadIdx.x] += buf[threadIdx.x + w];
+    if ((int)threadIdx.x < w) {
+      buf[threadIdx.x] += buf[threadIdx.x + w];
+      cnt[threadIdx.x] += cnt[threadIdx.x + w];
+    }
     __syncthreads();
   }
-  if (threadIdx.x == 0) *out = (float)(buf[0] * (double)scale);
+  if (threadIdx.x == 0) {
+    double scale = (double)a.scale;
+    if (a.mean_valid) scale = cnt[0] > 0 ? scale / (double)cnt[0] : 0.0;
+    if (a.out) *a.out = (float)(buf[0] * scale);
+    if (a.g_out) *a.g_out = (float)scale;
+  }
+}
+
+// dst = bf16(src), round to nearest even, 8 elements per thread and step.
+__global__ void __launch_bounds__(256) cast_bf16_kernel(const float* src, __bf16* dst, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * 256 * 8;
+  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8; i < n; i += stride) {
+    if (i + 8 <= n) {
+      const f32x4_t a = *reinterpret_cast<const f32x4_t*>(src + i);
+      const f32x4_t b = *reinterpret_cast<const f32x4_t*>(src + i + 4);
+      const bf16x8_t v = {(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3],
+                          (__bf16)b[0], (__bf16)b[1], (__bf16)b[2], (__bf16)b[3]};
+      *reinterpret_cast<bf16x8_t*>(dst + i) = v;
+    } else {
+      for (int64_t k = i; k < n; ++k) dst[k] = (__bf16)src[k];
+    }
+  }
 }
 
 // ================================================================ backward dZ
@@ -450,7 +482,7 @@ __device__ __forceinline__ void dz_tile(const DzArgs& a, int tm, int tn, char* l
   // exponent, each element costs one FMA and one exp2:
   //   g * exp(z - lse) = sign(g) * exp2(z * log2(e) + (log2|g| - lse * log2(e))).
   // Ignored tokens get a -inf bias (exactly 0), invalid targets a NaN bias.
-  const float g = a.grad_scale;
+  const float g = a.g_dev ? *a.g_dev : a.grad_scale;
   const float gsign = g < 0.f ? -1.f : 1.f;
   const float log2g = g == 0.f ? kNegInf : __log2f(fabsf(g));
   const bool tail = v0 + TL::BM > a.V;  // last vocab tile: rows past V are zero
@@ -733,8 +765,17 @@ hipError_t launch_fwd_merge(const MergeArgs& a, hipStream_t s) {
   return launch(fwd_merge_kernel, (int)((a.T + 255) / 256), 256, 0, s, a);
 }
 
-hipError_t launch_loss_sum(const float* loss, int64_t T, float scale, float* out, hipStream_t s) {
-  hipLaunchKernelGGL(loss_sum_kernel, dim3(1), dim3(1024), 0, s, loss, T, scale, out);
+hipError_t launch_loss_reduce(const ReduceArgs& a, hipStream_t s) {
+  return launch(loss_reduce_kernel, 1, 1024, 0, s, a);
+}
+
+hipError_t launch_cast_bf16(const float* src, void* dst, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n / 8 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(cast_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src,
+                     reinterpret_cast<__bf16*>(dst), n);
   return hipGetLastError();
 }
 

@@ -68,6 +68,7 @@ struct DzArgs {
   int64_t ldz;       // dZ row pitch (elements)
   int64_t ldz_cols;  // columns of each dZ row that this call writes
   float grad_scale;
+  const float* g_dev;  // when set, the gradient scale is read from here instead
   void* dz;
 };
 
@@ -109,7 +110,19 @@ struct TileInfo {
 TileInfo tile_info(bool bf16);
 hipError_t launch_fwd_sweep(const FwdArgs& a, bool bf16, int grid, hipStream_t s);
 hipError_t launch_fwd_merge(const MergeArgs& a, hipStream_t s);
-hipError_t launch_loss_sum(const float* loss, int64_t T, float scale, float* out, hipStream_t s);
+// Reduced loss and the matching gradient scale (see loss_reduce_kernel).
+struct ReduceArgs {
+  const float* loss;
+  const int64_t* y;  // read only for mean_valid
+  int64_t ignore_index;
+  int64_t T;
+  float scale;
+  int mean_valid;
+  float* out;    // optional
+  float* g_out;  // optional
+};
+hipError_t launch_loss_reduce(const ReduceArgs& a, hipStream_t s);
+hipError_t launch_cast_bf16(const float* src, void* dst, int64_t n, hipStream_t s);
 hipError_t launch_bwd_dz(const DzArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_dh(const DhArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_dw(const DwArgs& a, bool bf16, hipStream_t s);

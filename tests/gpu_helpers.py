@@ -74,9 +74,19 @@ def rel_fro(a, b):
     return float(d / nb)
 
 
-def compare(got, ref, dtype, what=("loss", "lse", "dH", "dW"), rows=None):
+def logit_tol(dtype, d, zmax):
+    """Loss/lse tolerance when the logits reach |z| = zmax: fp32 results carry
+    a rounding of about sqrt(d) ulps of |z| (sums of d terms in a kernel's own
+    order), which the fixed 1e-5 covers only for moderate logits; the bf16
+    tolerance is far above it."""
+    return TOL[dtype]["loss"] + (np.sqrt(d) * 2.0 ** -23 * zmax if dtype == wl.DTYPE_F32 else 0.0)
+
+
+def compare(got, ref, dtype, what=("loss", "lse", "dH", "dW"), rows=None, loss_tol=None):
     """Asserts the tolerances; returns the error figures."""
-    tol = TOL[dtype]
+    tol = dict(TOL[dtype])
+    if loss_tol is not None:
+        tol["loss"] = loss_tol
     errs = {}
     loss_ref, lse_ref = ref["loss"], ref["lse"]
     if "loss" in what:

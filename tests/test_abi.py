@@ -99,7 +99,7 @@ def test_plan_invariants_on_configs(lib, cfg):
     n_vt = -(-cfg.V // p.tile_v)
     assert p.fwd_splits * p.fwd_tiles_per_split >= n_vt
     assert (p.fwd_splits - 1) * p.fwd_tiles_per_split < n_vt
-    assert p.ws_bytes == max(p.fwd_ws_bytes, p.bwd_ws_bytes)
+    assert p.ws_bytes == max(p.fwd_ws_bytes, p.bwd_ws_bytes) + 256
 
 
 def test_plan_blocks_of_the_pages_shape(lib):
@@ -235,3 +235,21 @@ def test_token_logprobs_validation(lib):
     # nothing to score: no launch, no buffers needed
     assert _tok(lib, T=0, H=None, W=None, tok=None, out=None) == flce.FLCE_OK
     assert _tok(lib, K=0, H=None, W=None, tok=None, out=None) == flce.FLCE_OK
+
+
+def _fb(lib, plan, red=0, H=16, W=16, y=16, loss=16, lse=16, dH=16, dW=16, dWb=None, ws=16,
+        ws_bytes=1 << 40):
+    return lib.flce_forward_backward(ctypes.byref(plan), H, W, y, -100, red, 1.0, loss, lse, None,
+                                     dH, dW, 0, dWb, ws, ws_bytes, None)
+
+
+def test_forward_backward_validation(lib):
+    p = flce.flce_plan(100, 64, 1000, "bf16")
+    assert _fb(lib, flce.Plan()) == flce.FLCE_ERR_INVALID_ARG
+    assert _fb(lib, p, red=2) == flce.FLCE_ERR_INVALID_ARG
+    assert _fb(lib, p, red=-1) == flce.FLCE_ERR_INVALID_ARG
+    assert _fb(lib, p, dW=None) == flce.FLCE_ERR_INVALID_ARG
+    assert _fb(lib, p, loss=None) == flce.FLCE_ERR_INVALID_ARG
+    assert _fb(lib, p, dWb=24) == flce.FLCE_ERR_UNSUPPORTED
+    # the fused call needs the whole plan workspace (device scalars included)
+    assert _fb(lib, p, ws_bytes=p.ws_bytes - 1) == flce.FLCE_ERR_WORKSPACE

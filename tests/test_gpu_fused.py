@@ -1,0 +1,139 @@
+"""flce_forward_backward: the fused call against the separate calls (bit for
+bit) and the oracle; the device-side mean over non-ignored tokens; the bf16
+copy of dW; gradient accumulation across micro-batches."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import linear_cross_entropy_flce_amd as flce
+import oracle
+import workloads as wl
+from gpu_helpers import TOL, compare, device_inputs, log, logit_tol, max_abs
+
+pytestmark = pytest.mark.gpu
+IGN = wl.IGNORE_INDEX
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    flce.load()
+    yield
+    torch.cuda.empty_cache()
+
+
+def _np(t):
+    return t.float().cpu().numpy()
+
+
+def _separate(plan, H, W, y, scale, g):
+    red = torch.empty(1, dtype=torch.float32, device=W.device)
+    loss, lse, _ = flce.flce_forward(plan, H, W, y, IGN, scale, loss_reduced=red)
+    dH, dW = flce.flce_backward(plan, H, W, y, lse, IGN, g)
+    torch.cuda.synchronize()
+    return dict(loss=_np(loss), lse=_np(lse), red=_np(red), dH=_np(dH), dW=_np(dW))
+
+
+def _fused(plan, H, W, y, reduction, scale, **kw):
+    out = flce.flce_forward_backward(plan, H, W, y, IGN, reduction, scale, **kw)
+    torch.cuda.synchronize()
+    return {k: (_np(v) if v is not None else None) for k, v in out.items()}
+
+
+@pytest.mark.parametrize("dtype", [wl.DTYPE_F32, wl.DTYPE_BF16])
+@pytest.mark.parametrize("T,d,V,ign", [(257, 72, 32007, 0.1), (300, 136, 515, 0.3),
+                                       (1100, 64, 2049, 0.0)])
+def test_fused_equals_separate_and_oracle(T, d, V, ign, dtype):
+    inp = wl.make_inputs(T, d, V, dtype, seed=900 + T, sigma_w=0.5, ignore_frac=ign)
+    H, W, y = device_inputs(inp)
+    plan = flce.flce_plan(T, d, V, dtype)
+    n_valid = int((inp.y != IGN).sum())
+    # sum: g = scale
+    a = _fused(plan, H, W, y, "sum", 0.25)
+    b = _separate(plan, H, W, y, 0.25, 0.25)
+    for k in ("loss", "lse", "dH", "dW"):
+        assert np.array_equal(a[k], b[k], equal_nan=True), k
+    assert np.array_equal(a["loss_reduced"], b["red"])
+    # mean over the non-ignored tokens: g = 1 / N, counted on the device
+    g = float(np.float32(1.0 / n_valid))
+    a = _fused(plan, H, W, y, "mean_valid", 1.0)
+    b = _separate(plan, H, W, y, g, g)
+    for k in ("loss", "lse", "dH", "dW"):
+        assert np.array_equal(a[k], b[k], equal_nan=True), k
+    ref_loss, ref_lse, ref_dH, ref_dW = oracle.forward_backward(inp.H_f32(), inp.W_f32(), inp.y,
+                                                                IGN, 1.0 / n_valid)
+    tl = logit_tol(dtype, d, float(np.abs(oracle.logits(inp.H_f32(), inp.W_f32())).max()))
+    errs = compare(a, dict(loss=ref_loss, lse=ref_lse, dH=ref_dH, dW=ref_dW), dtype, loss_tol=tl)
+    mean = oracle.reduced_loss(ref_loss, 1.0 / n_valid)
+    assert abs(float(a["loss_reduced"][0]) - mean) <= tl
+    log("  mean_valid errors", errs)
+
+
+def test_mean_over_no_tokens_is_zero():
+    inp = wl.make_inputs(300, 64, 1000, wl.DTYPE_BF16, seed=5, sigma_w=0.5, ignore_frac=1.0)
+    H, W, y = device_inputs(inp)
+    plan = flce.flce_plan(inp.T, inp.d, inp.V, inp.dtype)
+    a = _fused(plan, H, W, y, "mean_valid", 1.0)
+    assert a["loss_reduced"][0] == 0.0
+    assert not np.any(a["dH"]) and not np.any(a["dW"])
+
+
+def test_dW_bf16_is_rounded_dW():
+    inp = wl.make_inputs(600, 128, 3001, wl.DTYPE_BF16, seed=6, sigma_w=0.5)
+    H, W, y = device_inputs(inp)
+    plan = flce.flce_plan(inp.T, inp.d, inp.V, inp.dtype)
+    dWb = torch.empty((inp.V, inp.d), dtype=torch.bfloat16, device=W.device)
+    out = flce.flce_forward_backward(plan, H, W, y, IGN, "sum", 1.0, dW_bf16=dWb)
+    torch.cuda.synchronize()
+    got = dWb.view(torch.int16).cpu().numpy().view(np.uint16)
+    want = wl.f32_to_bf16_bits(out["dW"].cpu().numpy())
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("dtype", [wl.DTYPE_F32, wl.DTYPE_BF16])
+def test_micro_batch_accumulation(dtype):
+    """Two micro-batches, the second accumulating into the first's fp32 dW,
+    give the gradient of the whole batch (sum reduction, one g)."""
+    inp = wl.make_inputs(800, 96, 5000, dtype, seed=7, sigma_w=0.5, ignore_frac=0.1)
+    H, W, y = device_inputs(inp)
+    g = 1.0 / inp.T
+    half = inp.T // 2
+    p1 = flce.flce_plan(half, inp.d, inp.V, dtype)
+    p2 = flce.flce_plan(inp.T - half, inp.d, inp.V, dtype)
+    dWb = torch.empty((inp.V, inp.d), dtype=torch.bfloat16, device=W.device)
+    o1 = flce.flce_forward_backward(p1, H[:half].contiguous(), W, y[:half].contiguous(), IGN,
+                                    "sum", g)
+    o2 = flce.flce_forward_backward(p2, H[half:].contiguous(), W, y[half:].contiguous(), IGN,
+                                    "sum", g, dW=o1["dW"], accumulate_dW=True, dW_bf16=dWb)
+    torch.cuda.synchronize()
+    ref_loss, ref_lse, ref_dH, ref_dW = oracle.forward_backward(inp.H_f32(), inp.W_f32(), inp.y,
+                                                                IGN, g)
+    dH = np.concatenate([_np(o1["dH"]), _np(o2["dH"])])
+    tl = logit_tol(dtype, inp.d, float(np.abs(oracle.logits(inp.H_f32(), inp.W_f32())).max()))
+    errs = compare(dict(loss=np.concatenate([_np(o1["loss"]), _np(o2["loss"])]),
+                        lse=np.concatenate([_np(o1["lse"]), _np(o2["lse"])]),
+                        dH=dH, dW=_np(o2["dW"])),
+                   dict(loss=ref_loss, lse=ref_lse, dH=ref_dH, dW=ref_dW), dtype, loss_tol=tl)
+    got = dWb.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, wl.f32_to_bf16_bits(_np(o2["dW"])))
+    log("  micro-batch errors", errs)
+
+
+@pytest.mark.timeout(600)
+def test_config2_mean_valid_fused():
+    """Config 2 (mean over valid tokens by reading): the fused call's device
+    count gives the same bits as the separate calls with g = 1/N_valid, which
+    the unfused config-2 test checks against the oracle."""
+    cfg = wl.CONFIGS[2]
+    inp = wl.config_inputs(cfg)
+    H, W, y = device_inputs(inp)
+    plan = flce.flce_plan(cfg.T, cfg.d, cfg.V, cfg.dtype)
+    ls, gs = cfg.scales()
+    a = _fused(plan, H, W, y, "mean_valid", 1.0)
+    b = _separate(plan, H, W, y, ls, gs)
+    for k in ("loss", "lse", "dH", "dW"):
+        assert np.array_equal(a[k], b[k], equal_nan=True), k
+    assert max_abs(a["loss_reduced"], b["red"]) <= 1e-6 * abs(float(b["red"][0]))
