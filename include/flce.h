@@ -75,7 +75,8 @@ typedef struct flce_plan {
   uint64_t fwd_ws_bytes;   /* per-split (max, sum) partials + target logits */
   uint64_t dz_ws_bytes;    /* the [bwd_block x bwd_slab] dZ tile buffer */
   uint64_t dh_acc_bytes;   /* fp32 dH accumulator, 0 when there is one slab */
-  uint64_t bwd_ws_bytes;   /* dz_ws_bytes + dh_acc_bytes */
+  uint64_t bwd_ws_bytes;   /* dz_ws_bytes + dh_acc_bytes + bwd_block x d elements (the
+                              token block's H, transposed for the dW contraction) */
   uint64_t ws_bytes;       /* max(fwd_ws_bytes, bwd_ws_bytes) + 256: enough for every call,
                               flce_forward_backward's device scalars included */
   uint64_t vocab_ws_cap;   /* the cap the planner honoured */
@@ -89,7 +90,8 @@ typedef struct flce_plan {
  *   T, d, V : problem size (see requirements above).
  *   dtype   : element type of H, W, dH.
  *   vocab_ws_cap_bytes : upper bound for the backward workspace (the dZ
- *             buffer plus the fp32 dH accumulator); 0 selects the default of
+ *             buffer, the fp32 dH accumulator and the transposed H block);
+ *             0 selects the default of
  *             950,000,000 bytes, keeping vocab-axis residency below 1 GB.
  *             Caps above 2^31 - 65536 bytes are lowered to that value.
  *   out     : host pointer, filled on success.

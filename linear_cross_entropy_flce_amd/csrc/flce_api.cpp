@@ -60,11 +60,11 @@ flce_status_t hip_fail(hipError_t e, const char* what) {
 // ------------------------------------------------------------ kernel timing
 enum KernelId {
   K_FWD_SWEEP, K_FWD_MERGE, K_LOSS_SUM, K_BWD_DZ, K_BWD_DH, K_BWD_DW, K_FILL, K_SHARD_MERGE,
-  K_TOKEN_LOGIT, K_CAST, K_COUNT
+  K_TOKEN_LOGIT, K_CAST, K_TRANSPOSE, K_COUNT
 };
 const char* const kKernelNames[K_COUNT] = {"fwd_sweep", "fwd_merge", "loss_sum",    "bwd_dz",
                                            "bwd_dh",    "bwd_dw",    "fill_zero",   "shard_merge",
-                                           "token_logit", "cast_bf16"};
+                                           "token_logit", "cast_bf16",   "transpose"};
 
 struct TimingRec {
   int kid;
@@ -155,6 +155,12 @@ double backward_cost(int64_t T, int64_t d, int64_t V, int64_t B, int64_t Vs,
 }  // namespace
 
 namespace {
+
+// The block's H transposed, read by the dW contraction as its K-contiguous
+// operand: B x d elements after the dH accumulator.
+uint64_t ht_bytes(int64_t B, int64_t d, int64_t esz) {
+  return flce::dw_uses_transposed_h() ? (uint64_t)(B * d * esz) : 0;
+}
 
 hipError_t launch_loss_sum(const float* loss, int64_t T, float scale, float* out, hipStream_t s) {
   flce::ReduceArgs r{loss, nullptr, 0, T, scale, 0, out, nullptr};
@@ -285,9 +291,19 @@ flce_status_t backward_impl(const flce_plan_t* plan, const void* H, const void* 
   float* dh_acc = p.dh_acc_bytes ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
                                                             p.dz_ws_bytes)
                                  : nullptr;
+  void* ht = flce::dw_uses_transposed_h()
+                 ? reinterpret_cast<char*>(ws) + p.dz_ws_bytes + p.dh_acc_bytes
+                 : nullptr;
   for (int64_t b = 0; b < p.n_blocks; ++b) {
     const int64_t t_begin = b * p.bwd_block;
     const int t_count = (int)(p.T - t_begin < p.bwd_block ? p.T - t_begin : p.bwd_block);
+    if (ht) {
+      Timed tm(s, K_TRANSPOSE, 0, 2.0 * t_count * p.d * p.elem_bytes);
+      e = flce::launch_transpose(reinterpret_cast<const char*>(H) + t_begin * p.d * p.elem_bytes,
+                                 t_count, (int)p.d, ht, p.bwd_block, bf16, s);
+      tm.done();
+      if (e != hipSuccess) return hip_fail(e, "H transpose launch");
+    }
     for (int64_t sl = 0; sl < p.n_slabs; ++sl) {
       const int64_t v_begin = sl * p.bwd_slab;
       const int v_count = (int)(p.V - v_begin < p.bwd_slab ? p.V - v_begin : p.bwd_slab);
@@ -346,6 +362,8 @@ flce_status_t backward_impl(const flce_plan_t* plan, const void* H, const void* 
       flce::DwArgs w;
       w.dz = dz;
       w.H = H;
+      w.Ht = ht;
+      w.ldht = p.bwd_block;
       w.ldz = p.bwd_slab;
       w.T = p.T;
       w.d = (int)p.d;
@@ -484,7 +502,8 @@ flce_status_t flce_plan(int64_t T, int64_t d, int64_t V, flce_dtype_t dtype, uin
     double best_cost = 0;
     for (int64_t Vs = ti.logit_bm; Vs <= Vfull; Vs += ti.logit_bm) {
       const int64_t slabs = cdiv(V, Vs);
-      const uint64_t need = (uint64_t)(B * Vs * esz) + (slabs > 1 ? (uint64_t)(B * d * 4) : 0);
+      const uint64_t need = (uint64_t)(B * Vs * esz) + (slabs > 1 ? (uint64_t)(B * d * 4) : 0) +
+                            ht_bytes(B, d, esz);
       if (need > cap) break;  // need grows with Vs
       const double c = backward_cost(T > 0 ? T : 1, d, V, B, Vs, ti);
       if (best_B == 0 || c < best_cost * (1 - 1e-9)) {
@@ -505,7 +524,7 @@ flce_status_t flce_plan(int64_t T, int64_t d, int64_t V, flce_dtype_t dtype, uin
   p.n_slabs = best_slabs;
   p.dz_ws_bytes = (uint64_t)(best_B * best_Vs * esz);
   p.dh_acc_bytes = best_slabs > 1 ? (uint64_t)(best_B * d * 4) : 0;
-  p.bwd_ws_bytes = p.dz_ws_bytes + p.dh_acc_bytes;
+  p.bwd_ws_bytes = p.dz_ws_bytes + p.dh_acc_bytes + ht_bytes(best_B, d, esz);
   p.ws_bytes = (p.fwd_ws_bytes > p.bwd_ws_bytes ? p.fwd_ws_bytes : p.bwd_ws_bytes) + kScalarBytes;
   p.vocab_ws_cap = cap;
   p.naive_logits_bytes = (uint64_t)T * (uint64_t)V * (uint64_t)esz;

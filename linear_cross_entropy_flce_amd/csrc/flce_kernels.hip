@@ -115,13 +115,18 @@ struct DhCfg<float> {
 };
 template <typename E>
 struct DwCfg;
+#ifndef FLCE_DW_HT
+#define FLCE_DW_HT 1
+#endif
+// dW^T = H[block]^T dZ: A = the block's H transposed into the workspace
+// (K-contiguous) when FLCE_DW_HT, else H itself (MN-contiguous).
 template <>
 struct DwCfg<__bf16> {
-  using T = BigTile<__bf16, false, false, FLCE_DW_NS, FLCE_DW_KB, FLCE_DW_DMA>;
+  using T = BigTile<__bf16, FLCE_DW_HT != 0, false, FLCE_DW_NS, FLCE_DW_KB, FLCE_DW_DMA>;
 };
 template <>
 struct DwCfg<float> {
-  using T = SmallTile<float, false, false, FLCE_DW_NS>;
+  using T = SmallTile<float, FLCE_DW_HT != 0, false, FLCE_DW_NS>;
 };
 
 __device__ __forceinline__ uint32_t clamp_bytes(int64_t b) {
@@ -634,11 +639,19 @@ __global__ void __launch_bounds__(DwCfg<E>::T::NT, 1) bwd_dw_kernel(DwArgs a) {
   const int64_t vl0 = (int64_t)tn * TL::BN;  // vocab within slab
 
   Operand A, B;
-  A.rs = make_rsrc(a.H, clamp_bytes(a.T * a.d * ESZ));
-  A.off = (uint32_t)((a.t_begin * a.d + n0) * ESZ);
-  A.ld_bytes = (uint32_t)(a.d * ESZ);
-  A.rows = a.t_count;
-  A.cols = (int)min<int64_t>(TL::BM, a.d - n0);
+  if constexpr (TL::kAKC) {  // H^T of the block: [d][ldht]
+    A.rs = make_rsrc(a.Ht, clamp_bytes((int64_t)a.d * a.ldht * ESZ));
+    A.off = (uint32_t)(n0 * a.ldht * ESZ);
+    A.ld_bytes = (uint32_t)(a.ldht * ESZ);
+    A.rows = (int)min<int64_t>(TL::BM, a.d - n0);
+    A.cols = a.t_count;
+  } else {  // H rows of the block
+    A.rs = make_rsrc(a.H, clamp_bytes(a.T * a.d * ESZ));
+    A.off = (uint32_t)((a.t_begin * a.d + n0) * ESZ);
+    A.ld_bytes = (uint32_t)(a.d * ESZ);
+    A.rows = a.t_count;
+    A.cols = (int)min<int64_t>(TL::BM, a.d - n0);
+  }
   B.rs = make_rsrc(a.dz, clamp_bytes((int64_t)a.t_count * a.ldz * ESZ));
   B.off = (uint32_t)(vl0 * ESZ);
   B.ld_bytes = (uint32_t)(a.ldz * ESZ);
@@ -654,6 +667,9 @@ __global__ void __launch_bounds__(DwCfg<E>::T::NT, 1) bwd_dw_kernel(DwArgs a) {
     tile.load_acc_t(dw, a.d, n_rows, v_cols);
   else
     tile.zero();
+  // a block holds at least one token; without this the compiler keeps a copy
+  // of the preloaded tile (spilled) for a K loop that runs zero times
+  __builtin_assume(a.t_count > 0);
   tile.mainloop(A, B, a.t_count, lds);
 
   // each lane holds four consecutive hidden units of one vocab row per quad
@@ -683,6 +699,42 @@ __global__ void __launch_bounds__(256) fill_zero_kernel(float* p, int64_t n) {
     } else {
       for (int64_t k = i; k < n; ++k) p[k] = 0.f;
     }
+  }
+}
+
+// ================================================================= transpose
+// dst[c * ld_dst + r] = src[r * cols + c] for r < rows, c < cols (cols a
+// multiple of 8, ld_dst of 8): 64 x 64 tiles through LDS, 16-byte global
+// loads and stores.
+template <typename E>
+__global__ void __launch_bounds__(256) transpose_kernel(const E* src, int64_t rows, int cols,
+                                                        E* dst, int64_t ld_dst) {
+  constexpr int CW = 16 / (int)sizeof(E);  // elements per 16 bytes
+  __shared__ E tile[64][64 + CW];
+  const int64_t r0 = (int64_t)blockIdx.y * 64;
+  const int c0 = blockIdx.x * 64;
+  constexpr int CPR = 64 / CW;  // 16-byte chunks per tile row
+  for (int i = threadIdx.x; i < 64 * CPR; i += 256) {
+    const int r = i / CPR, ch = i % CPR;
+    const int64_t gr = r0 + r;
+    const int gc = c0 + ch * CW;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (gr < rows && gc < cols) v = *reinterpret_cast<const u32x4_t*>(src + gr * cols + gc);
+    const E* e = reinterpret_cast<const E*>(&v);
+#pragma unroll
+    for (int k = 0; k < CW; ++k) tile[r][ch * CW + k] = e[k];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * CPR; i += 256) {
+    const int c = i / CPR, ch = i % CPR;
+    const int gc = c0 + c;
+    const int64_t gr = r0 + ch * CW;
+    if (gc >= cols || gr >= rows) continue;
+    u32x4_t v;
+    E* e = reinterpret_cast<E*>(&v);
+#pragma unroll
+    for (int k = 0; k < CW; ++k) e[k] = tile[ch * CW + k][c];
+    *reinterpret_cast<u32x4_t*>(dst + gc * ld_dst + gr) = v;
   }
 }
 
@@ -778,6 +830,23 @@ hipError_t launch_cast_bf16(const float* src, void* dst, int64_t n, hipStream_t 
                      reinterpret_cast<__bf16*>(dst), n);
   return hipGetLastError();
 }
+
+hipError_t launch_transpose(const void* src, int64_t rows, int cols, void* dst, int64_t ld_dst,
+                            bool bf16, hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+  if (bf16)
+    hipLaunchKernelGGL(transpose_kernel<__bf16>, grid, dim3(256), 0, s,
+                       reinterpret_cast<const __bf16*>(src), rows, cols,
+                       reinterpret_cast<__bf16*>(dst), ld_dst);
+  else
+    hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, s,
+                       reinterpret_cast<const float*>(src), rows, cols,
+                       reinterpret_cast<float*>(dst), ld_dst);
+  return hipGetLastError();
+}
+
+bool dw_uses_transposed_h() { return FLCE_DW_HT != 0; }
 
 hipError_t launch_token_logit(const TokenArgs& a, bool bf16, hipStream_t s) {
   const int grid = (int)((a.T + 3) / 4);

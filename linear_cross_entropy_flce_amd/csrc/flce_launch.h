@@ -90,6 +90,8 @@ struct DhArgs {
 struct DwArgs {
   const void* dz;
   const void* H;
+  const void* Ht;   // the block's H transposed, [d][ldht] (when the kernel reads it)
+  int64_t ldht;
   int64_t ldz;
   int64_t T;
   int d;
@@ -140,6 +142,10 @@ struct TokenArgs {
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 hipError_t launch_token_logit(const TokenArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_transpose(const void* src, int64_t rows, int cols, void* dst, int64_t ld_dst,
+                            bool bf16, hipStream_t s);
+// whether bwd_dw reads the block's H transposed (a workspace of B x d elements)
+bool dw_uses_transposed_h();
 hipError_t launch_shard_merge(const ShardMergeArgs& a, hipStream_t s);
 
 }  // namespace flce

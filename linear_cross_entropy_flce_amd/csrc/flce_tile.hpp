@@ -122,55 +122,30 @@ struct Tile {
 
   f32x16_t acc[MI][NI];
 
-  // acc = C[tile] for a row-major fp32 matrix (row pitch ldc elements) whose
-  // tile origin is `c`; `rows` x `cols` of it are valid.  The buffer resource
-  // ends at the last valid element, so rows past `rows` read as 0; columns
-  // past `cols` may read neighbouring elements of valid rows, which only
-  // reach accumulators that are never stored.  Loads are issued before the K
-  // loop, whose prologue hides their latency.
-  __device__ __forceinline__ void load_acc(const float* c, int64_t ldc, int rows, int cols) {
-    const int wave = threadIdx.x >> 6;
-    const int wm = wave / WN, wn = wave % WN;
-    const int64_t bytes = rows > 0 && cols > 0 ? ((int64_t)(rows - 1) * ldc + cols) * 4 : 0;
-    const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(c, (uint32_t)(bytes > 0x7fffffff ? 0x7fffffff : bytes));
-    const uint32_t ld4 = (uint32_t)ldc * 4u;
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < NI; ++j) {
-        const uint32_t base = (uint32_t)row_of(wm, i, 0) * ld4 + (uint32_t)col_of(wn, j) * 4u;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t soff = (uint32_t)(8 * (r >> 2) + (r & 3)) * ld4;
-          acc[i][j][r] = __builtin_bit_cast(
-              float, __builtin_amdgcn_raw_buffer_load_b32(rs, base, __builtin_amdgcn_readfirstlane(soff), 0));
-        }
-      }
-  }
-
   // acc = C[tile] for a matrix stored transposed: tile element (row, col) is
   // c[col * ldc + row], with `rows` x `cols` of the tile valid and `rows` a
-  // multiple of 4.  Each lane's four consecutive rows are one 16-byte load.
-  // The buffer resource ends at the last valid element, so columns past
-  // `cols` read as 0.
+  // multiple of 4.  Each lane's four consecutive rows are one 16-byte load;
+  // the row offsets of the (i, quad) blocks are immediates on one per-column
+  // address register.  The buffer resource ends at the last valid element, so
+  // columns past `cols` read as 0.
   __device__ __forceinline__ void load_acc_t(const float* c, int64_t ldc, int rows, int cols) {
-    const int wave = threadIdx.x >> 6;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wm = wave / WN, wn = wave % WN;
     const int64_t bytes = rows > 0 && cols > 0 ? ((int64_t)(cols - 1) * ldc + rows) * 4 : 0;
     const __amdgpu_buffer_rsrc_t rs =
         make_rsrc(c, (uint32_t)(bytes > 0x7fffffff ? 0x7fffffff : bytes));
     const uint32_t ld4 = (uint32_t)ldc * 4u;
+    const int row0 = wm * WTM + 4 * (lane >> 5);  // this lane's first row
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
-      const uint32_t base = (uint32_t)col_of(wn, j) * ld4;
+      const uint32_t vo = (uint32_t)col_of(wn, j) * ld4 + (uint32_t)row0 * 4u;
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int row = row_of(wm, i, 4 * q);
-          const f32x4_t v = __builtin_bit_cast(
-              f32x4_t, buffer_load16(rs, row < rows ? base + (uint32_t)row * 4u : kOOB));
+          const int dr = i * 32 + 8 * q;
+          const uint32_t off = rows >= BM || row0 + dr < rows ? vo + (uint32_t)dr * 4u : kOOB;
+          const f32x4_t v = __builtin_bit_cast(f32x4_t, buffer_load16(rs, off));
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = v[e];
         }
