@@ -98,7 +98,8 @@ def measured_traffic(kernel: str, workload: str):
 
 
 TRAFFIC_SOURCES = ["linear_cross_entropy_flce_amd/csrc/flce_kernels.hip",
-                   "linear_cross_entropy_flce_amd/csrc/flce_tile.hpp"]
+                   "linear_cross_entropy_flce_amd/csrc/flce_tile.hpp",
+                   "linear_cross_entropy_flce_amd/csrc/flce_api.cpp"]
 
 
 def summarize_traffic(fetch_csv: str, write_csv: str, cfetch_csv: str, cwrite_csv: str,
