@@ -82,11 +82,14 @@ def logit_tol(dtype, d, zmax):
     return TOL[dtype]["loss"] + (np.sqrt(d) * 2.0 ** -23 * zmax if dtype == wl.DTYPE_F32 else 0.0)
 
 
-def compare(got, ref, dtype, what=("loss", "lse", "dH", "dW"), rows=None, loss_tol=None):
+def compare(got, ref, dtype, what=("loss", "lse", "dH", "dW"), rows=None, loss_tol=None,
+            grad_tol=None):
     """Asserts the tolerances; returns the error figures."""
     tol = dict(TOL[dtype])
     if loss_tol is not None:
         tol["loss"] = loss_tol
+    if grad_tol is not None:
+        tol["grad"] = grad_tol
     errs = {}
     loss_ref, lse_ref = ref["loss"], ref["lse"]
     if "loss" in what:

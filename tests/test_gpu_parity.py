@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import workloads as wl
-from gpu_helpers import TOL, compare, device_inputs, log, max_abs, rel_fro, run_gpu
+from gpu_helpers import TOL, compare, device_inputs, log, logit_tol, max_abs, rel_fro, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -121,6 +121,22 @@ def test_large_logits_running_max():
         u = (2.0 ** -8 if dtype == wl.DTYPE_BF16 else 0.0) + 8 * ulp
         bound = 2 * c[0] * u + tg * np.abs(ref["dH"][:, 0]).max()
         assert max_abs(got["dH"][:, 0], ref["dH"][:, 0]) <= bound
+
+
+@pytest.mark.parametrize("dtype", [wl.DTYPE_F32, wl.DTYPE_BF16])
+def test_long_hidden(dtype):
+    """d = 16,384 (a long K loop for the logit tiles, long rows for every
+    operand offset) with a ragged token count and vocabulary."""
+    T, d, V = 300, 16384, 700
+    inp = wl.make_inputs(T, d, V, dtype, seed=37, sigma_w=0.02, ignore_frac=0.1)
+    got = run_gpu(inp, grad_scale=0.5)
+    # fp32: sums of 16,384 terms round by ~sqrt(d) ulps of |z|; the same
+    # absolute error in z - lse is the relative error of each dZ entry
+    zmax = float(np.abs(oracle.logits(inp.H_f32(), inp.W_f32())).max())
+    extra = logit_tol(dtype, d, zmax) - TOL[dtype]["loss"]
+    errs = compare(got, _ref(inp, 0.5), dtype, loss_tol=TOL[dtype]["loss"] + extra,
+                   grad_tol=TOL[dtype]["grad"] + extra)
+    log("  errors", errs)
 
 
 @pytest.mark.parametrize("dtype", [wl.DTYPE_F32, wl.DTYPE_BF16])
