@@ -75,8 +75,9 @@ typedef struct flce_plan {
   uint64_t fwd_ws_bytes;   /* per-split (max, sum) partials + target logits */
   uint64_t dz_ws_bytes;    /* the [bwd_block x bwd_slab] dZ tile buffer */
   uint64_t dh_acc_bytes;   /* fp32 dH accumulator, 0 when there is one slab */
-  uint64_t bwd_ws_bytes;   /* dz_ws_bytes + dh_acc_bytes + bwd_block x d elements (the
-                              token block's H, transposed for the dW contraction) */
+  uint64_t bwd_ws_bytes;   /* dz_ws_bytes + dh_acc_bytes + 2 x bwd_block x d elements (the
+                              token block's H as rows and transposed) + the compacted
+                              token order (4 bytes per token) and counters */
   uint64_t ws_bytes;       /* max(fwd_ws_bytes, bwd_ws_bytes) + 256: enough for every call,
                               flce_forward_backward's device scalars included */
   uint64_t vocab_ws_cap;   /* the cap the planner honoured */
@@ -90,8 +91,8 @@ typedef struct flce_plan {
  *   T, d, V : problem size (see requirements above).
  *   dtype   : element type of H, W, dH.
  *   vocab_ws_cap_bytes : upper bound for the backward workspace (the dZ
- *             buffer, the fp32 dH accumulator and the transposed H block);
- *             0 selects the default of
+ *             buffer, the fp32 dH accumulator, the gathered H block and the
+ *             token order); 0 selects the default of
  *             950,000,000 bytes, keeping vocab-axis residency below 1 GB.
  *             Caps above 2^31 - 65536 bytes are lowered to that value.
  *   out     : host pointer, filled on success.
@@ -116,6 +117,9 @@ flce_status_t flce_forward(const flce_plan_t* plan, const void* H, const void* W
                            void* stream);
 
 /* flce_backward -- dH and dW of grad_scale * sum_i loss_i.
+ *   Ignored tokens contribute nothing (their dZ rows are zero), so the
+ *   backward compacts the other tokens on the device (ascending order) and
+ *   runs its contractions over them only; their dH rows are written as 0.
  *   lse [T]  : the forward's output for the same H, W (its normaliser lets
  *              the recompute form softmax without a running max).
  *   grad_scale : scalar multiplying every dZ element (1/N for a mean).

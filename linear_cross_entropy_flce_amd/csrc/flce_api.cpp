@@ -66,11 +66,12 @@ flce_status_t hip_fail(hipError_t e, const char* what) {
 // ------------------------------------------------------------ kernel timing
 enum KernelId {
   K_FWD_SWEEP, K_FWD_MERGE, K_LOSS_SUM, K_BWD_DZ, K_BWD_DH, K_BWD_DW, K_FILL, K_SHARD_MERGE,
-  K_TOKEN_LOGIT, K_CAST, K_TRANSPOSE, K_COUNT
+  K_TOKEN_LOGIT, K_CAST, K_TRANSPOSE, K_COMPACT, K_COUNT
 };
 const char* const kKernelNames[K_COUNT] = {"fwd_sweep", "fwd_merge", "loss_sum",    "bwd_dz",
                                            "bwd_dh",    "bwd_dw",    "fill_zero",   "shard_merge",
-                                           "token_logit", "cast_bf16",   "transpose"};
+                                           "token_logit", "cast_bf16",   "gather_h",
+                                           "compact"};
 
 struct TimingRec {
   int kid;
@@ -162,10 +163,23 @@ double backward_cost(int64_t T, int64_t d, int64_t V, int64_t B, int64_t Vs,
 
 namespace {
 
-// The block's H transposed, read by the dW contraction as its K-contiguous
-// operand: B x d elements after the dH accumulator.
-uint64_t ht_bytes(int64_t B, int64_t d, int64_t esz) {
-  return flce::dw_uses_transposed_h() ? (uint64_t)(B * d * esz) : 0;
+// Backward workspace after the dZ buffer and the dH accumulator: the token
+// block's H gathered in the compacted order, transposed (Ht, the dW
+// contraction's K-contiguous operand) and as rows (Hc, the recompute's), then
+// the compacted token order (idx [T]), the per-chunk counts of the
+// compaction and the count of non-ignored tokens.
+struct BwdTail {
+  uint64_t ht, hc, idx, cnt, tv, bytes;  // offsets from the end of dh_acc
+};
+BwdTail bwd_tail(int64_t T, int64_t B, int64_t d, int64_t esz) {
+  BwdTail t;
+  t.ht = 0;
+  t.hc = (uint64_t)(B * d * esz);
+  t.idx = 2 * t.hc;
+  t.cnt = t.idx + (uint64_t)round_up(T * 4, 256);
+  t.tv = t.cnt + (uint64_t)round_up(flce::compact_chunks(T) * 4, 256);
+  t.bytes = t.tv + 256;
+  return t;
 }
 
 hipError_t launch_loss_sum(const float* loss, int64_t T, float scale, float* out, hipStream_t s) {
@@ -297,33 +311,44 @@ flce_status_t backward_impl(const flce_plan_t* plan, const void* H, const void* 
   float* dh_acc = p.dh_acc_bytes ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
                                                             p.dz_ws_bytes)
                                  : nullptr;
-  void* ht = flce::dw_uses_transposed_h()
-                 ? reinterpret_cast<char*>(ws) + p.dz_ws_bytes + p.dh_acc_bytes
-                 : nullptr;
+  char* tail = reinterpret_cast<char*>(ws) + p.dz_ws_bytes + p.dh_acc_bytes;
+  const BwdTail tl = bwd_tail(p.T, p.bwd_block, p.d, p.elem_bytes);
+  void* ht = tail + tl.ht;
+  void* hc = tail + tl.hc;
+  int* idx = reinterpret_cast<int*>(tail + tl.idx);
+  int* tv = reinterpret_cast<int*>(tail + tl.tv);
+  {
+    // the non-ignored tokens in ascending order; dH rows of the others are 0
+    Timed tm(s, K_COMPACT, 0, p.T * 8.0 * 2 + p.T * 8.0);
+    e = flce::launch_compact(tg.y, tg.ignore_index, p.T, reinterpret_cast<int*>(tail + tl.cnt),
+                             idx, tv, s);
+    if (e == hipSuccess) e = flce::launch_zero_rows(dH, idx, tv, p.T, (int)p.d, bf16, s);
+    tm.done();
+    if (e != hipSuccess) return hip_fail(e, "token compaction launch");
+  }
   for (int64_t b = 0; b < p.n_blocks; ++b) {
     const int64_t t_begin = b * p.bwd_block;
+    // at most this many tokens (the device knows how many are not ignored)
     const int t_count = (int)(p.T - t_begin < p.bwd_block ? p.T - t_begin : p.bwd_block);
-    if (ht) {
-      Timed tm(s, K_TRANSPOSE, 0, 2.0 * t_count * p.d * p.elem_bytes);
-      e = flce::launch_transpose(reinterpret_cast<const char*>(H) + t_begin * p.d * p.elem_bytes,
-                                 t_count, (int)p.d, ht, p.bwd_block, bf16, s);
+    const flce::TokBlock blk{idx, tv, t_begin, (int)p.bwd_block};
+    {
+      Timed tm(s, K_TRANSPOSE, 0, 3.0 * p.bwd_block * p.d * p.elem_bytes);
+      e = flce::launch_gather_block(H, blk, (int)p.d, hc, ht, bf16, s);
       tm.done();
-      if (e != hipSuccess) return hip_fail(e, "H transpose launch");
+      if (e != hipSuccess) return hip_fail(e, "H gather launch");
     }
     for (int64_t sl = 0; sl < p.n_slabs; ++sl) {
       const int64_t v_begin = sl * p.bwd_slab;
       const int v_count = (int)(p.V - v_begin < p.bwd_slab ? p.V - v_begin : p.bwd_slab);
 
       flce::DzArgs z;
-      z.H = H;
+      z.Hc = hc;
       z.W = W;
       z.tg = tg;
       z.lse = lse;
-      z.T = p.T;
       z.d = (int)p.d;
       z.V = (int)p.V;
-      z.t_begin = t_begin;
-      z.t_count = t_count;
+      z.blk = blk;
       z.v_begin = v_begin;
       z.n_vtiles = (int)cdiv(v_count, ti.logit_bm);
       z.n_ttiles = (int)cdiv(t_count, ti.logit_bn);
@@ -345,8 +370,7 @@ flce_status_t backward_impl(const flce_plan_t* plan, const void* H, const void* 
       h.ldz = p.bwd_slab;
       h.d = (int)p.d;
       h.V = (int)p.V;
-      h.t_begin = t_begin;
-      h.t_count = t_count;
+      h.blk = blk;
       h.v_begin = v_begin;
       h.k_count = v_count;
       h.n_mtiles = (int)cdiv(t_count, ti.dh_bm);
@@ -367,14 +391,11 @@ flce_status_t backward_impl(const flce_plan_t* plan, const void* H, const void* 
 
       flce::DwArgs w;
       w.dz = dz;
-      w.H = H;
       w.Ht = ht;
       w.ldht = p.bwd_block;
       w.ldz = p.bwd_slab;
-      w.T = p.T;
       w.d = (int)p.d;
-      w.t_begin = t_begin;
-      w.t_count = t_count;
+      w.blk = blk;
       w.v_begin = v_begin;
       w.v_count = v_count;
       w.n_mtiles = (int)cdiv(p.d, ti.dw_bm);
@@ -509,7 +530,7 @@ flce_status_t flce_plan(int64_t T, int64_t d, int64_t V, flce_dtype_t dtype, uin
     for (int64_t Vs = ti.logit_bm; Vs <= Vfull; Vs += ti.logit_bm) {
       const int64_t slabs = cdiv(V, Vs);
       const uint64_t need = (uint64_t)(B * Vs * esz) + (slabs > 1 ? (uint64_t)(B * d * 4) : 0) +
-                            ht_bytes(B, d, esz);
+                            bwd_tail(T, B, d, esz).bytes;
       if (need > cap) break;  // need grows with Vs
       const double c = backward_cost(T > 0 ? T : 1, d, V, B, Vs, ti);
       if (best_B == 0 || c < best_cost * (1 - 1e-9)) {
@@ -530,7 +551,7 @@ flce_status_t flce_plan(int64_t T, int64_t d, int64_t V, flce_dtype_t dtype, uin
   p.n_slabs = best_slabs;
   p.dz_ws_bytes = (uint64_t)(best_B * best_Vs * esz);
   p.dh_acc_bytes = best_slabs > 1 ? (uint64_t)(best_B * d * 4) : 0;
-  p.bwd_ws_bytes = p.dz_ws_bytes + p.dh_acc_bytes + ht_bytes(best_B, d, esz);
+  p.bwd_ws_bytes = p.dz_ws_bytes + p.dh_acc_bytes + bwd_tail(T, best_B, d, esz).bytes;
   p.ws_bytes = (p.fwd_ws_bytes > p.bwd_ws_bytes ? p.fwd_ws_bytes : p.bwd_ws_bytes) + kScalarBytes;
   p.vocab_ws_cap = cap;
   p.naive_logits_bytes = (uint64_t)T * (uint64_t)V * (uint64_t)esz;

@@ -115,19 +115,23 @@ struct DhCfg<float> {
 };
 template <typename E>
 struct DwCfg;
-#ifndef FLCE_DW_HT
-#define FLCE_DW_HT 1
-#endif
-// dW^T = H[block]^T dZ: A = the block's H transposed into the workspace
-// (K-contiguous) when FLCE_DW_HT, else H itself (MN-contiguous).
+// dW^T = Ht[block] dZ: A = the token block's H, transposed into the workspace
+// (K-contiguous); B = dZ (MN-contiguous).
 template <>
 struct DwCfg<__bf16> {
-  using T = BigTile<__bf16, FLCE_DW_HT != 0, false, FLCE_DW_NS, FLCE_DW_KB, FLCE_DW_DMA>;
+  using T = BigTile<__bf16, true, false, FLCE_DW_NS, FLCE_DW_KB, FLCE_DW_DMA>;
 };
 template <>
 struct DwCfg<float> {
-  using T = SmallTile<float, FLCE_DW_HT != 0, false, FLCE_DW_NS>;
+  using T = SmallTile<float, true, false, FLCE_DW_NS>;
 };
+
+// Tokens in a block of the compacted order (0 when it lies past the last
+// non-ignored token).
+__device__ __forceinline__ int block_count(const TokBlock& b) {
+  const int64_t n = (int64_t)*b.tv - b.t_begin;
+  return n <= 0 ? 0 : (n < b.t_max ? (int)n : b.t_max);
+}
 
 __device__ __forceinline__ uint32_t clamp_bytes(int64_t b) {
   return (uint32_t)(b < 0 ? 0 : (b > 0x7fffffffLL ? 0x7fffffffLL : b));
@@ -466,6 +470,8 @@ __device__ __forceinline__ void dz_tile(const DzArgs& a, int tm, int tn, char* l
   const int wm = wave / TL::WN, wn = wave % TL::WN;
   const int64_t v0 = a.v_begin + (int64_t)tm * TL::BM;  // global vocab id of tile row 0
   const int64_t tl0 = (int64_t)tn * TL::BN;             // token within the block
+  const int t_count = block_count(a.blk);
+  if (tl0 >= t_count) return;
 
   Operand A, B;
   A.rs = make_rsrc(a.W, clamp_bytes((int64_t)a.V * a.d * ESZ));
@@ -473,10 +479,10 @@ __device__ __forceinline__ void dz_tile(const DzArgs& a, int tm, int tn, char* l
   A.ld_bytes = (uint32_t)(a.d * ESZ);
   A.rows = (int)max<int64_t>(0, min<int64_t>(TL::BM, a.V - v0));
   A.cols = a.d;
-  B.rs = make_rsrc(a.H, clamp_bytes(a.T * a.d * ESZ));
-  B.off = (uint32_t)((a.t_begin + tl0) * a.d * ESZ);
+  B.rs = make_rsrc(a.Hc, clamp_bytes((int64_t)a.blk.t_max * a.d * ESZ));
+  B.off = (uint32_t)(tl0 * a.d * ESZ);
   B.ld_bytes = (uint32_t)(a.d * ESZ);
-  B.rows = (int)min<int64_t>(TL::BN, a.t_count - tl0);
+  B.rows = (int)min<int64_t>(TL::BN, t_count - tl0);
   B.cols = a.d;
 
   TL tile;
@@ -497,8 +503,8 @@ __device__ __forceinline__ void dz_tile(const DzArgs& a, int tm, int tn, char* l
   for (int j = 0; j < TL::NI; ++j) {
     const int c = TL::col_of(wn, j);
     const int64_t tl = tl0 + c;
-    const bool col_ok = tl < a.t_count;
-    const int64_t t = a.t_begin + (col_ok ? tl : 0);
+    const bool col_ok = tl < t_count;
+    const int64_t t = a.blk.idx[a.blk.t_begin + (col_ok ? tl : 0)];  // the token itself
     const int code = target_code(a.tg, t, a.V);
     const float lse_t = a.lse[t];
     const float bias = code == kIgnored ? kNegInf
@@ -551,7 +557,7 @@ __device__ __forceinline__ void dz_tile(const DzArgs& a, int tm, int tn, char* l
     }
   }
   if constexpr (ESZ == 2) store_dz_tile<TL>(tile, lds, dz, a.ldz, v0 - a.v_begin, a.ldz_cols,
-                                            tl0, a.t_count, wm, wn);
+                                            tl0, t_count, wm, wn);
 }
 
 template <typename E>
@@ -579,12 +585,14 @@ __global__ void __launch_bounds__(DhCfg<E>::T::NT, 1) bwd_dh_kernel(DhArgs a) {
   const int wm = wave / TL::WN, wn = wave % TL::WN;
   const int64_t tl0 = (int64_t)tm * TL::BM;  // token within block
   const int64_t n0 = (int64_t)tn * TL::BN;   // hidden index
+  const int t_count = block_count(a.blk);
+  if (tl0 >= t_count) return;
 
   Operand A, B;
-  A.rs = make_rsrc(a.dz, clamp_bytes((int64_t)a.t_count * a.ldz * ESZ));
+  A.rs = make_rsrc(a.dz, clamp_bytes((int64_t)t_count * a.ldz * ESZ));
   A.off = (uint32_t)(tl0 * a.ldz * ESZ);
   A.ld_bytes = (uint32_t)(a.ldz * ESZ);
-  A.rows = (int)min<int64_t>(TL::BM, a.t_count - tl0);
+  A.rows = (int)min<int64_t>(TL::BM, t_count - tl0);
   A.cols = a.k_count;
   B.rs = make_rsrc(a.W, clamp_bytes((int64_t)a.V * a.d * ESZ));
   B.off = (uint32_t)((a.v_begin * a.d + n0) * ESZ);
@@ -605,14 +613,15 @@ __global__ void __launch_bounds__(DhCfg<E>::T::NT, 1) bwd_dh_kernel(DhArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t tl = tl0 + TL::row_of(wm, i, r);
-        if (tl >= a.t_count) continue;
+        if (tl >= t_count) continue;
         float v = tile.acc[i][j][r];
         float* accp = a.dh_acc + tl * a.d + n;
         if (a.mode == 1 || a.mode == 2) v += *accp;
         if (a.mode == 0 || a.mode == 1) {
           *accp = v;
         } else {
-          E* out = reinterpret_cast<E*>(a.dH) + (a.t_begin + tl) * a.d + n;
+          const int64_t t = a.blk.idx[a.blk.t_begin + tl];  // the token's own row
+          E* out = reinterpret_cast<E*>(a.dH) + t * a.d + n;
           *out = (E)v;
         }
       }
@@ -638,24 +647,19 @@ __global__ void __launch_bounds__(DwCfg<E>::T::NT, 1) bwd_dw_kernel(DwArgs a) {
   const int64_t n0 = (int64_t)tm * TL::BM;   // hidden
   const int64_t vl0 = (int64_t)tn * TL::BN;  // vocab within slab
 
+  const int t_count = block_count(a.blk);  // K
+  if (t_count == 0 && a.accumulate) return;  // nothing to add
+
   Operand A, B;
-  if constexpr (TL::kAKC) {  // H^T of the block: [d][ldht]
-    A.rs = make_rsrc(a.Ht, clamp_bytes((int64_t)a.d * a.ldht * ESZ));
-    A.off = (uint32_t)(n0 * a.ldht * ESZ);
-    A.ld_bytes = (uint32_t)(a.ldht * ESZ);
-    A.rows = (int)min<int64_t>(TL::BM, a.d - n0);
-    A.cols = a.t_count;
-  } else {  // H rows of the block
-    A.rs = make_rsrc(a.H, clamp_bytes(a.T * a.d * ESZ));
-    A.off = (uint32_t)((a.t_begin * a.d + n0) * ESZ);
-    A.ld_bytes = (uint32_t)(a.d * ESZ);
-    A.rows = a.t_count;
-    A.cols = (int)min<int64_t>(TL::BM, a.d - n0);
-  }
-  B.rs = make_rsrc(a.dz, clamp_bytes((int64_t)a.t_count * a.ldz * ESZ));
+  A.rs = make_rsrc(a.Ht, clamp_bytes((int64_t)a.d * a.ldht * ESZ));
+  A.off = (uint32_t)(n0 * a.ldht * ESZ);
+  A.ld_bytes = (uint32_t)(a.ldht * ESZ);
+  A.rows = (int)min<int64_t>(TL::BM, a.d - n0);
+  A.cols = t_count;
+  B.rs = make_rsrc(a.dz, clamp_bytes((int64_t)t_count * a.ldz * ESZ));
   B.off = (uint32_t)(vl0 * ESZ);
   B.ld_bytes = (uint32_t)(a.ldz * ESZ);
-  B.rows = a.t_count;
+  B.rows = t_count;
   B.cols = (int)min<int64_t>(TL::BN, a.ldz - vl0);
 
   const int n_rows = (int)min<int64_t>(TL::BM, a.d - n0);  // a multiple of 8
@@ -667,10 +671,14 @@ __global__ void __launch_bounds__(DwCfg<E>::T::NT, 1) bwd_dw_kernel(DwArgs a) {
     tile.load_acc_t(dw, a.d, n_rows, v_cols);
   else
     tile.zero();
-  // a block holds at least one token; without this the compiler keeps a copy
-  // of the preloaded tile (spilled) for a K loop that runs zero times
-  __builtin_assume(a.t_count > 0);
-  tile.mainloop(A, B, a.t_count, lds);
+  // An empty block (every token ignored) only overwrites with zeros.  Past
+  // this branch the K loop runs at least once, which the compiler must know:
+  // otherwise it keeps a spilled copy of the preloaded tile for a loop that
+  // runs zero times.
+  if (t_count > 0) {
+    __builtin_assume(t_count > 0);
+    tile.mainloop(A, B, t_count, lds);
+  }
 
   // each lane holds four consecutive hidden units of one vocab row per quad
 #pragma unroll
@@ -702,24 +710,115 @@ __global__ void __launch_bounds__(256) fill_zero_kernel(float* p, int64_t n) {
   }
 }
 
-// ================================================================= transpose
-// dst[c * ld_dst + r] = src[r * cols + c] for r < rows, c < cols (cols a
-// multiple of 8, ld_dst of 8): 64 x 64 tiles through LDS, 16-byte global
-// loads and stores.
+// ================================================================ compaction
+// The backward skips ignored tokens: their dZ rows are zero, so they add
+// nothing to dH or dW.  Three passes give a deterministic order: counts per
+// chunk of kChunk tokens, an exclusive scan of the counts, then each chunk
+// writes its non-ignored tokens (ascending) from its offset and its ignored
+// ones after all non-ignored tokens.
+constexpr int kChunk = 4096;  // tokens per workgroup: 256 threads x 16
+
+__global__ void __launch_bounds__(256) compact_count_kernel(const int64_t* y, int64_t ignore,
+                                                            int64_t T, int* cnt) {
+  __shared__ int red[256];
+  const int64_t t0 = (int64_t)blockIdx.x * kChunk + threadIdx.x * 16;
+  int c = 0;
+  for (int k = 0; k < 16; ++k) c += (t0 + k < T && y[t0 + k] != ignore) ? 1 : 0;
+  red[threadIdx.x] = c;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) cnt[blockIdx.x] = red[0];
+}
+
+// One workgroup: exclusive scan of n counts in place, the total into *tv.
+__global__ void __launch_bounds__(1024) compact_scan_kernel(int* cnt, int64_t n, int* tv) {
+  __shared__ int buf[1024];
+  int carry = 0;
+  for (int64_t base = 0; base < n; base += 1024) {
+    const int64_t i = base + threadIdx.x;
+    const int v = i < n ? cnt[i] : 0;
+    buf[threadIdx.x] = v;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {  // inclusive scan
+      const int add = (int)threadIdx.x >= o ? buf[threadIdx.x - o] : 0;
+      __syncthreads();
+      buf[threadIdx.x] += add;
+      __syncthreads();
+    }
+    if (i < n) cnt[i] = carry + buf[threadIdx.x] - v;
+    carry += buf[1023];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *tv = carry;
+}
+
+__global__ void __launch_bounds__(256) compact_scatter_kernel(const int64_t* y, int64_t ignore,
+                                                              int64_t T, const int* off,
+                                                              const int* tv, int* idx) {
+  __shared__ int buf[256];
+  const int64_t t0 = (int64_t)blockIdx.x * kChunk + threadIdx.x * 16;
+  unsigned valid = 0;
+  int c = 0;
+  for (int k = 0; k < 16; ++k)
+    if (t0 + k < T && y[t0 + k] != ignore) {
+      valid |= 1u << k;
+      ++c;
+    }
+  buf[threadIdx.x] = c;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const int add = (int)threadIdx.x >= o ? buf[threadIdx.x - o] : 0;
+    __syncthreads();
+    buf[threadIdx.x] += add;
+    __syncthreads();
+  }
+  int64_t vpos = (int64_t)off[blockIdx.x] + buf[threadIdx.x] - c;  // valid tokens before t0
+  int64_t ipos = *tv + (t0 - vpos);                                // ignored tokens before t0
+  for (int k = 0; k < 16; ++k) {
+    if (t0 + k >= T) break;
+    if (valid >> k & 1u) idx[vpos++] = (int)(t0 + k);
+    else idx[ipos++] = (int)(t0 + k);
+  }
+}
+
+// Zeros the dH rows of the ignored tokens, 16 bytes per item.
 template <typename E>
-__global__ void __launch_bounds__(256) transpose_kernel(const E* src, int64_t rows, int cols,
-                                                        E* dst, int64_t ld_dst) {
-  constexpr int CW = 16 / (int)sizeof(E);  // elements per 16 bytes
-  __shared__ E tile[64][64 + CW];
-  const int64_t r0 = (int64_t)blockIdx.y * 64;
-  const int c0 = blockIdx.x * 64;
+__global__ void __launch_bounds__(256) zero_rows_kernel(E* dH, const int* idx, const int* tv,
+                                                        int64_t T, int d) {
+  constexpr int CW = 16 / (int)sizeof(E);
+  const int cpr = d / CW;
+  const int64_t n = (T - *tv) * cpr;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t row = idx[*tv + i / cpr];
+    *reinterpret_cast<u32x4_t*>(dH + row * d + (i % cpr) * CW) = u32x4_t{0u, 0u, 0u, 0u};
+  }
+}
+
+// A token block of H gathered from the compacted order: Hc[r] = H[idx[t_begin
+// + r]] and Ht[c][r] = Hc[r][c] for r < t_max (zero rows past the block's
+// token count); 64 x 64 tiles through LDS, 16-byte loads and stores.
+template <typename E>
+__global__ void __launch_bounds__(256) gather_block_kernel(const E* H, TokBlock blk, int d, E* Hc,
+                                                           E* Ht) {
+  constexpr int CW = 16 / (int)sizeof(E);
   constexpr int CPR = 64 / CW;  // 16-byte chunks per tile row
+  __shared__ E tile[64][64 + CW];
+  const int count = block_count(blk);
+  const int r0 = blockIdx.y * 64;
+  const int c0 = blockIdx.x * 64;
   for (int i = threadIdx.x; i < 64 * CPR; i += 256) {
     const int r = i / CPR, ch = i % CPR;
-    const int64_t gr = r0 + r;
     const int gc = c0 + ch * CW;
+    if (r0 + r >= blk.t_max || gc >= d) continue;
     u32x4_t v = {0u, 0u, 0u, 0u};
-    if (gr < rows && gc < cols) v = *reinterpret_cast<const u32x4_t*>(src + gr * cols + gc);
+    if (r0 + r < count) {
+      const int64_t t = blk.idx[blk.t_begin + r0 + r];
+      v = *reinterpret_cast<const u32x4_t*>(H + t * d + gc);
+    }
+    *reinterpret_cast<u32x4_t*>(Hc + (int64_t)(r0 + r) * d + gc) = v;
     const E* e = reinterpret_cast<const E*>(&v);
 #pragma unroll
     for (int k = 0; k < CW; ++k) tile[r][ch * CW + k] = e[k];
@@ -728,13 +827,13 @@ __global__ void __launch_bounds__(256) transpose_kernel(const E* src, int64_t ro
   for (int i = threadIdx.x; i < 64 * CPR; i += 256) {
     const int c = i / CPR, ch = i % CPR;
     const int gc = c0 + c;
-    const int64_t gr = r0 + ch * CW;
-    if (gc >= cols || gr >= rows) continue;
+    const int gr = r0 + ch * CW;
+    if (gc >= d || gr >= blk.t_max) continue;
     u32x4_t v;
     E* e = reinterpret_cast<E*>(&v);
 #pragma unroll
     for (int k = 0; k < CW; ++k) e[k] = tile[ch * CW + k][c];
-    *reinterpret_cast<u32x4_t*>(dst + gc * ld_dst + gr) = v;
+    *reinterpret_cast<u32x4_t*>(Ht + (int64_t)gc * blk.t_max + gr) = v;
   }
 }
 
@@ -831,22 +930,53 @@ hipError_t launch_cast_bf16(const float* src, void* dst, int64_t n, hipStream_t 
   return hipGetLastError();
 }
 
-hipError_t launch_transpose(const void* src, int64_t rows, int cols, void* dst, int64_t ld_dst,
-                            bool bf16, hipStream_t s) {
-  if (rows <= 0 || cols <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
-  if (bf16)
-    hipLaunchKernelGGL(transpose_kernel<__bf16>, grid, dim3(256), 0, s,
-                       reinterpret_cast<const __bf16*>(src), rows, cols,
-                       reinterpret_cast<__bf16*>(dst), ld_dst);
-  else
-    hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, s,
-                       reinterpret_cast<const float*>(src), rows, cols,
-                       reinterpret_cast<float*>(dst), ld_dst);
+int64_t compact_chunks(int64_t T) { return (T + kChunk - 1) / kChunk; }
+
+hipError_t launch_compact(const int64_t* y, int64_t ignore_index, int64_t T, int* cnt, int* idx,
+                          int* tv, hipStream_t s) {
+  const int64_t n = compact_chunks(T);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(compact_count_kernel, dim3((unsigned)n), dim3(256), 0, s, y, ignore_index, T,
+                     cnt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(compact_scan_kernel, dim3(1), dim3(1024), 0, s, cnt, n, tv);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(compact_scatter_kernel, dim3((unsigned)n), dim3(256), 0, s, y, ignore_index,
+                     T, (const int*)cnt, (const int*)tv, idx);
   return hipGetLastError();
 }
 
-bool dw_uses_transposed_h() { return FLCE_DW_HT != 0; }
+hipError_t launch_zero_rows(void* dH, const int* idx, const int* tv, int64_t T, int d, bool bf16,
+                            hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const int64_t items = T * (int64_t)(d / (bf16 ? 8 : 4));
+  int64_t blocks = (items + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  if (bf16)
+    hipLaunchKernelGGL(zero_rows_kernel<__bf16>, dim3((unsigned)blocks), dim3(256), 0, s,
+                       reinterpret_cast<__bf16*>(dH), idx, tv, T, d);
+  else
+    hipLaunchKernelGGL(zero_rows_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s,
+                       reinterpret_cast<float*>(dH), idx, tv, T, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_block(const void* H, const TokBlock& blk, int d, void* Hc, void* Ht,
+                               bool bf16, hipStream_t s) {
+  if (blk.t_max <= 0 || d <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((d + 63) / 64), (unsigned)((blk.t_max + 63) / 64));
+  if (bf16)
+    hipLaunchKernelGGL(gather_block_kernel<__bf16>, grid, dim3(256), 0, s,
+                       reinterpret_cast<const __bf16*>(H), blk, d, reinterpret_cast<__bf16*>(Hc),
+                       reinterpret_cast<__bf16*>(Ht));
+  else
+    hipLaunchKernelGGL(gather_block_kernel<float>, grid, dim3(256), 0, s,
+                       reinterpret_cast<const float*>(H), blk, d, reinterpret_cast<float*>(Hc),
+                       reinterpret_cast<float*>(Ht));
+  return hipGetLastError();
+}
 
 hipError_t launch_token_logit(const TokenArgs& a, bool bf16, hipStream_t s) {
   const int grid = (int)((a.T + 3) / 4);

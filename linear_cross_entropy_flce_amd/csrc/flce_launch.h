@@ -54,15 +54,25 @@ struct ShardMergeArgs {
   float* lse;
 };
 
+// The backward works on the non-ignored tokens only: compacted in ascending
+// order, idx[p] is the token at compacted position p (positions [*tv, T)
+// hold the ignored tokens).  A token block is compacted positions
+// [t_begin, t_begin + t_max); it holds block_count() tokens, which only the
+// device knows.
+struct TokBlock {
+  const int* idx;
+  const int* tv;
+  int64_t t_begin;
+  int t_max;
+};
+
 struct DzArgs {
-  const void* H;
+  const void* Hc;  // the block's H rows, compacted: [t_max][d]
   const void* W;
   Targets tg;
   const float* lse;
-  int64_t T;
   int d, V;
-  int64_t t_begin;  // first token of the block
-  int t_count;      // tokens in the block
+  TokBlock blk;
   int64_t v_begin;  // first vocab id of the slab
   int n_vtiles, n_ttiles;
   int64_t ldz;       // dZ row pitch (elements)
@@ -77,8 +87,7 @@ struct DhArgs {
   const void* W;
   int64_t ldz;
   int d, V;
-  int64_t t_begin;
-  int t_count;
+  TokBlock blk;
   int64_t v_begin;
   int k_count;  // vocab rows in the slab (K)
   int n_mtiles, n_ntiles;
@@ -89,14 +98,11 @@ struct DhArgs {
 
 struct DwArgs {
   const void* dz;
-  const void* H;
-  const void* Ht;   // the block's H transposed, [d][ldht] (when the kernel reads it)
+  const void* Ht;   // the block's H rows transposed, [d][ldht]
   int64_t ldht;
   int64_t ldz;
-  int64_t T;
   int d;
-  int64_t t_begin;
-  int t_count;   // K
+  TokBlock blk;  // K = block_count()
   int64_t v_begin;
   int v_count;   // N
   int n_mtiles, n_ntiles;  // hidden tiles, vocab tiles
@@ -142,10 +148,18 @@ struct TokenArgs {
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 hipError_t launch_token_logit(const TokenArgs& a, bool bf16, hipStream_t s);
-hipError_t launch_transpose(const void* src, int64_t rows, int cols, void* dst, int64_t ld_dst,
-                            bool bf16, hipStream_t s);
-// whether bwd_dw reads the block's H transposed (a workspace of B x d elements)
-bool dw_uses_transposed_h();
+// Compaction of the non-ignored tokens: idx [T], *tv, with cnt [n] scratch
+// (n = compact_chunks(T)).
+int64_t compact_chunks(int64_t T);
+hipError_t launch_compact(const int64_t* y, int64_t ignore_index, int64_t T, int* cnt, int* idx,
+                          int* tv, hipStream_t s);
+// dH rows of the ignored tokens (compacted positions [*tv, T)) set to zero.
+hipError_t launch_zero_rows(void* dH, const int* idx, const int* tv, int64_t T, int d, bool bf16,
+                            hipStream_t s);
+// One token block of H gathered: Hc [t_max][d] rows and Ht [d][t_max], zero
+// past the block's token count.
+hipError_t launch_gather_block(const void* H, const TokBlock& blk, int d, void* Hc, void* Ht,
+                               bool bf16, hipStream_t s);
 hipError_t launch_shard_merge(const ShardMergeArgs& a, hipStream_t s);
 
 }  // namespace flce
