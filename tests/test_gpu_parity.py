@@ -157,6 +157,34 @@ def test_several_blocks_and_slabs(dtype):
 
 
 @pytest.mark.parametrize("dtype", [wl.DTYPE_F32, wl.DTYPE_BF16])
+@pytest.mark.parametrize("pattern", ["suffix", "prefix", "alternate"])
+def test_ignored_tokens_across_blocks(pattern, dtype):
+    """The backward runs over the non-ignored tokens only, compacted into
+    token blocks; with small blocks, whole blocks fall empty (suffix), the
+    compacted order starts late in the batch (prefix) or interleaves
+    (alternate), and accumulate_dW must still see every block's part."""
+    T, d, V = 1500, 64, 900
+    inp = wl.make_inputs(T, d, V, dtype, seed=41, sigma_w=0.4)
+    if pattern == "suffix":
+        inp.y[300:] = IGN
+    elif pattern == "prefix":
+        inp.y[:1200] = IGN
+    else:
+        inp.y[::2] = IGN
+    esz = 4 if dtype == wl.DTYPE_F32 else 2
+    tile_v = 128 if dtype == wl.DTYPE_F32 else 256
+    cap = 512 * (d * 4 + tile_v * esz)
+    base = np.random.default_rng(3).standard_normal((V, d)).astype(np.float32)
+    got = run_gpu(inp, grad_scale=0.5, cap=cap, accumulate_dW=True, dW_init=base)
+    plan = got["plan"]
+    assert plan.n_blocks >= 4
+    ref = _ref(inp, 0.5)
+    ref["dW"] = ref["dW"] + base
+    compare(got, ref, dtype)
+    assert np.all(got["dH"][inp.y == IGN] == 0.0)
+
+
+@pytest.mark.parametrize("dtype", [wl.DTYPE_F32, wl.DTYPE_BF16])
 def test_accumulate_dW(dtype):
     inp = wl.make_inputs(300, 48, 700, dtype, seed=19, sigma_w=0.4)
     base = np.random.default_rng(0).standard_normal((700, 48)).astype(np.float32)
