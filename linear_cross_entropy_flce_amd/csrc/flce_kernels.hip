@@ -9,15 +9,22 @@
 //
 // Kernels (the method is section 3 of "Long-Sequence MoE RL Training: From
 // First Principles to MI300X"):
-//   fwd_sweep   logits tile + running max / log-sum-exp over the workgroup's
-//               vocab range, target logit captured from the fp32 accumulator;
-//               writes per-split (max, sum) partials and z_target.
-//   fwd_merge   merges the splits in ascending order: lse, loss.
-//   loss_reduce fixed-order double-precision sum (and count) for the reduced loss.
-//   bwd_dz      recomputed logits tile -> dZ = g * (exp(z - lse) - onehot),
-//               stored (bf16 or fp32) to the [block x slab] workspace.
-//   bwd_dh      dH_block (+)= dZ W_slab   (fp32 accumulate, cast at the end).
-//   bwd_dw      dW_slab (+)= dZ^T H_block (fp32, deterministic block order).
+//   fwd_sweep    logits tile + running max / log-sum-exp over the workgroup's
+//                vocab range, target logit captured from the fp32 accumulator;
+//                writes per-split (max, sum) partials and z_target.
+//   fwd_merge    merges the splits in ascending order: lse, loss (or, for a
+//                vocab shard, the shard's lse and target logit).
+//   shard_merge  lse and loss from several shards' statistics.
+//   loss_reduce  fixed-order double-precision sum (and count) for the reduced loss.
+//   compact_*    the backward's token order: non-ignored tokens first, ascending.
+//   zero_rows    dH rows of the ignored tokens.
+//   gather_block one token block of H in that order, as rows and transposed.
+//   bwd_dz       recomputed logits tile -> dZ = g * (exp(z - lse) - onehot),
+//                stored (bf16 or fp32) to the [block x slab] workspace.
+//   bwd_dh       dH_block (+)= dZ W_slab   (fp32 accumulate, cast at the end).
+//   bwd_dw       dW_slab^T (+)= H_block^T dZ (fp32, deterministic block order).
+//   token_logit  gathered h . w minus lse for given tokens (scoring).
+//   cast_bf16    optional bf16 copy of dW.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -101,8 +108,7 @@ struct LogitCfg<float> {
   using T = SmallTile<float, true, true, FLCE_LOGIT_NS>;
 };
 
-// dH (A = dZ K-contiguous, B = W MN-contiguous) and dW^T (A = H, B = dZ, both
-// MN-contiguous).
+// dH (A = dZ K-contiguous, B = W MN-contiguous).
 template <typename E>
 struct DhCfg;
 template <>
