@@ -76,7 +76,6 @@ def measured_traffic(kernel: str, workload: str):
     or None when there is none for this workload or the kernel sources have
     changed since the counters were taken."""
     import glob
-    import hashlib
     for path in glob.glob(os.path.join(ROOT, "profiles", "traffic_*.json")):
         try:
             rec = json.load(open(path))
@@ -84,17 +83,47 @@ def measured_traffic(kernel: str, workload: str):
             continue
         if not rec.get("workload", "").startswith(workload):
             continue
-        h = hashlib.sha256()
-        for f in rec.get("source_files", []):
-            try:
-                h.update(open(os.path.join(ROOT, f), "rb").read())
-            except OSError:
-                return None
-        if h.hexdigest() != rec.get("source_sha256"):
+        try:
+            digest = code_digest(rec.get("source_files", []))
+        except OSError:
+            return None
+        if digest != rec.get("source_sha256"):
             return None
         k = rec.get("per_launch", {}).get(kernel)
         return None if k is None else int(k["traffic_bytes"])
     return None
+
+
+def code_digest(files) -> str:
+    """SHA-256 of the C/C++ sources with comments removed and whitespace runs
+    collapsed, so that the recorded traffic survives edits that leave the
+    compiled code as it was."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        src = open(os.path.join(ROOT, f), encoding="utf-8").read()
+        out, i, n = [], 0, len(src)
+        while i < n:
+            c = src[i]
+            if c == "/" and src.startswith("//", i):
+                j = src.find("\n", i)
+                i = n if j < 0 else j
+            elif c == "/" and src.startswith("/*", i):
+                j = src.find("*/", i + 2)
+                i = n if j < 0 else j + 2
+                out.append(" ")
+            elif c in "\"'":
+                j = i + 1
+                while j < n and src[j] != c:
+                    j += 2 if src[j] == "\\" else 1
+                out.append(src[i:j + 1])
+                i = j + 1
+            else:
+                out.append(c)
+                i += 1
+        h.update(" ".join("".join(out).split()).encode())
+        h.update(b"\0")
+    return h.hexdigest()
 
 
 TRAFFIC_SOURCES = ["linear_cross_entropy_flce_amd/csrc/flce_kernels.hip",
@@ -109,7 +138,6 @@ def summarize_traffic(fetch_csv: str, write_csv: str, cfetch_csv: str, cwrite_cs
     the same two counters over --copy-calibration, whose copy kernel moves a
     known number of bytes and so gives each counter's scale."""
     import csv
-    import hashlib
     import re
     from collections import defaultdict
 
@@ -152,9 +180,6 @@ def summarize_traffic(fetch_csv: str, write_csv: str, cfetch_csv: str, cwrite_cs
         if n:
             agg[n]["nw"] += 1
             agg[n]["write"] += v
-    h = hashlib.sha256()
-    for f in TRAFFIC_SOURCES:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
     per = {}
     for n, a in agg.items():
         if not a["n"] or not a["nw"]:
@@ -168,10 +193,10 @@ def summarize_traffic(fetch_csv: str, write_csv: str, cfetch_csv: str, cwrite_cs
         "about": "HBM traffic per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per "
                  "dispatch), each divided by the value the same counter reads per byte of a plain "
                  "1 GiB device copy (bench.py --copy-calibration 1024). Valid only while the "
-                 "kernel sources hash to source_sha256.",
+                 "kernel sources, comments and whitespace aside, hash to source_sha256.",
         "workload": workload,
         "source_files": TRAFFIC_SOURCES,
-        "source_sha256": h.hexdigest(),
+        "source_sha256": code_digest(TRAFFIC_SOURCES),
         "calibration": {"copy_bytes": cal_bytes,
                         "fetch_counter_bytes_per_byte": round(f_per_byte, 4),
                         "write_counter_bytes_per_byte": round(w_per_byte, 4)},
