@@ -450,6 +450,16 @@ def main():
     log(f"  {ms:.2f} ms/step (wall {wall / args.steps * 1e3:.2f} ms), {value:.1f} TFLOP/s, "
         f"{100 * value / peak:.1f}% of {peak} TFLOP/s")
     step_kernel_ms = sum(k["total_ms"] for k in kernels.values()) / args.steps
+    # The backward skips ignored tokens, but the library counts each launch's
+    # flops over its token block's capacity; the algorithmic flops of the
+    # contraction kernels per step are 2*T_valid*d*V each (2*T*d*V forward).
+    t_valid = int((inp.y != wl.IGNORE_INDEX).sum())
+    alg_step = {"fwd_sweep": 2.0 * T * d * V, "bwd_dz": 2.0 * t_valid * d * V,
+                "bwd_dh": 2.0 * t_valid * d * V, "bwd_dw": 2.0 * t_valid * d * V}
+    for name, k in kernels.items():
+        if name in alg_step:
+            k["flops"] = alg_step[name] * args.steps
+    effective = (2.0 * T * d * V + 6.0 * t_valid * d * V) / (ms / 1e3) / 1e12
     for name, k in kernels.items():
         tf = k["flops"] / (k["total_ms"] / 1e3) / 1e12 if k["total_ms"] else 0.0
         log(f"  {name:10s} launches {k['launches']:5d}  avg {k['total_ms'] / k['launches']:8.3f} ms"
@@ -490,6 +500,11 @@ def main():
                    "targets": cfg.targets, "ignored_tokens": cfg.n_ignored,
                    "grad_scale": gs, "parallelism": "single GPU"},
         "mfma_peak_frac": round(value / peak, 4),
+        # 2*T*d*V + 6*T_valid*d*V per step: the work left once the backward
+        # skips ignored tokens (equal to value when none are ignored)
+        "effective_tflops": round(effective, 2),
+        "valid_tokens": t_valid,
+        "ignored_tokens_skipped_in_backward": True,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "memory": {"peak_allocated_bytes": int(peak_mem),
