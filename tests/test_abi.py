@@ -73,6 +73,13 @@ def test_plan_rejects(lib, args, status):
     assert flce.last_error()
 
 
+def test_plan_accepts_dW_beyond_2GiB(lib):
+    # bf16 W of 1.02 GiB plans; its fp32 dW (2.03 GiB) is addressed per tile
+    st, p = flce.flce_plan_status(320, 3584, 152064, flce.FLCE_BF16)
+    assert st == flce.FLCE_OK
+    assert 152064 * 3584 * 4 > 2 ** 31
+
+
 def test_plan_null_out(lib):
     assert lib.flce_plan(10, 128, 1000, 1, 0, None) == flce.FLCE_ERR_INVALID_ARG
 

@@ -251,6 +251,27 @@ def test_config2_full():
     log("  errors", errs)
 
 
+@pytest.mark.timeout(600)
+def test_dW_beyond_2GiB():
+    """A large-vocabulary shape whose fp32 dW (152,064 x 3,584 x 4 bytes =
+    2.03 GiB) reaches past 2^31 bytes while W and H stay below it: every
+    output against the oracle, and the dW rows that start past the 2 GiB
+    byte offset on their own."""
+    T, d, V = 320, 3584, 152064
+    log(f"dW beyond 2 GiB: T={T} d={d} V={V} bf16")
+    inp = wl.make_inputs(T, d, V, wl.DTYPE_BF16, seed=4242, sigma_w=0.02, ignore_frac=0.1)
+    g = 1.0 / T
+    got = run_gpu(inp, loss_scale=g, grad_scale=g)
+    log("  oracle")
+    ref = _ref(inp, g)
+    errs = compare(got, ref, wl.DTYPE_BF16)
+    first = -(-(1 << 31) // (d * 4))  # first dW row whose bytes start at or past 2^31
+    assert first < V
+    tail = rel_fro(got["dW"][first:], ref["dW"][first:])
+    log("  errors", errs, f"dW rows {first}..{V - 1}: {tail:.3e}")
+    assert tail <= TOL[wl.DTYPE_BF16]["grad"]
+
+
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("ci", [3, 4])
 def test_config_sampled(ci):
