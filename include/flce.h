@@ -77,12 +77,19 @@ typedef struct flce_plan {
   uint64_t dh_acc_bytes;   /* fp32 dH accumulator, 0 when there is one slab */
   uint64_t bwd_ws_bytes;   /* dz_ws_bytes + dh_acc_bytes + 2 x bwd_block x d elements (the
                               token block's H as rows and transposed) + the compacted
-                              token order (4 bytes per token) and counters */
+                              token order (4 bytes per token) and counters
+                              + dh_split_bytes */
   uint64_t ws_bytes;       /* max(fwd_ws_bytes, bwd_ws_bytes) + 256: enough for every call,
                               flce_forward_backward's device scalars included */
   uint64_t vocab_ws_cap;   /* the cap the planner honoured */
   /* context: bytes of one materialised [T x V] logits copy in the dtype */
   uint64_t naive_logits_bytes;
+  /* fp32 partial tiles that let dH split its vocab (K) loop when a token
+   * block has too few tiles to occupy every compute unit (small T or d, or a
+   * block thinned by ignored tokens); the device picks the split from the
+   * block's token count.  0 when they do not fit under the cap beside the
+   * chosen block and slab (dH then never splits). */
+  uint64_t dh_split_bytes;
   uint32_t magic;          /* set by flce_plan; checked by the other calls */
   uint32_t reserved;
 } flce_plan_t;

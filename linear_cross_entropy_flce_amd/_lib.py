@@ -42,7 +42,7 @@ class Plan(ctypes.Structure):
         ("fwd_ws_bytes", ctypes.c_uint64), ("dz_ws_bytes", ctypes.c_uint64),
         ("dh_acc_bytes", ctypes.c_uint64), ("bwd_ws_bytes", ctypes.c_uint64),
         ("ws_bytes", ctypes.c_uint64), ("vocab_ws_cap", ctypes.c_uint64),
-        ("naive_logits_bytes", ctypes.c_uint64),
+        ("naive_logits_bytes", ctypes.c_uint64), ("dh_split_bytes", ctypes.c_uint64),
         ("magic", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
     ]
 

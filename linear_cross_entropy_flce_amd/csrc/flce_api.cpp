@@ -66,12 +66,12 @@ flce_status_t hip_fail(hipError_t e, const char* what) {
 // ------------------------------------------------------------ kernel timing
 enum KernelId {
   K_FWD_SWEEP, K_FWD_MERGE, K_LOSS_SUM, K_BWD_DZ, K_BWD_DH, K_BWD_DW, K_FILL, K_SHARD_MERGE,
-  K_TOKEN_LOGIT, K_CAST, K_TRANSPOSE, K_COMPACT, K_COUNT
+  K_TOKEN_LOGIT, K_CAST, K_TRANSPOSE, K_COMPACT, K_DH_REDUCE, K_COUNT
 };
 const char* const kKernelNames[K_COUNT] = {"fwd_sweep", "fwd_merge", "loss_sum",    "bwd_dz",
                                            "bwd_dh",    "bwd_dw",    "fill_zero",   "shard_merge",
                                            "token_logit", "cast_bf16",   "gather_h",
-                                           "compact"};
+                                           "compact", "dh_reduce"};
 
 struct TimingRec {
   int kid;
@@ -317,6 +317,7 @@ flce_status_t backward_impl(const flce_plan_t* plan, const void* H, const void* 
   void* hc = tail + tl.hc;
   int* idx = reinterpret_cast<int*>(tail + tl.idx);
   int* tv = reinterpret_cast<int*>(tail + tl.tv);
+  float* dh_part = p.dh_split_bytes ? reinterpret_cast<float*>(tail + tl.bytes) : nullptr;
   {
     // the non-ignored tokens in ascending order; dH rows of the others are 0
     Timed tm(s, K_COMPACT, 0, p.T * 8.0 * 2 + p.T * 8.0);
@@ -381,6 +382,7 @@ flce_status_t backward_impl(const flce_plan_t* plan, const void* H, const void* 
       else h.mode = 2;
       h.dh_acc = dh_acc;
       h.dH = dH;
+      h.part = dh_part;
       Timed t_dh(s, K_BWD_DH, 2.0 * tc * dd * vc,
                  tc * vc * esz + vc * dd * esz +
                      tc * dd * (h.mode == 1 || h.mode == 2 ? 4.0 : 0.0) +
@@ -388,6 +390,14 @@ flce_status_t backward_impl(const flce_plan_t* plan, const void* H, const void* 
       e = flce::launch_bwd_dh(h, bf16, s);
       t_dh.done();
       if (e != hipSuccess) return hip_fail(e, "dH launch");
+      if (dh_part) {
+        // sums the parts when the device split the K loop (reads them all
+        // once, then the mode's accumulator and dH traffic)
+        Timed t_red(s, K_DH_REDUCE, 0, tc * dd * 4.0 * 2);
+        e = flce::launch_bwd_dh_reduce(h, bf16, s);
+        t_red.done();
+        if (e != hipSuccess) return hip_fail(e, "dH reduce launch");
+      }
 
       flce::DwArgs w;
       w.dz = dz;
@@ -521,23 +531,37 @@ flce_status_t flce_plan(int64_t T, int64_t d, int64_t V, flce_dtype_t dtype, uin
   // which some vocab slab fits under the cap, then the slab width that
   // minimises the modelled time (backward_cost): a dZ buffer of B x Vs plus
   // the fp32 dH accumulator when the vocab needs several slabs.
+  //
+  // dH's tile grid is (B / dh_bm) x (d / dh_bn).  When a full block has at
+  // most half as many tiles as the GPU has compute units, dH will split its
+  // K loop, so the partial tiles it needs are part of `need` in a first
+  // search; a second search without them serves caps too small for both.
   const int64_t Tr = round_up(T > 0 ? T : 1, ti.logit_bn);
   const int64_t Vfull = round_up(V, ti.logit_bm);
+  const int64_t dh_nt = cdiv(d, ti.dh_bn);
+  const uint64_t split = (uint64_t)flce::dh_split_slots() * ti.dh_bm * ti.dh_bn * 4;
   int64_t best_B = 0, best_Vs = 0, best_slabs = 0;
-  for (int64_t B = (Tr < kMaxBlock ? Tr : kMaxBlock); B >= ti.logit_bn && best_B == 0;
-       B -= ti.logit_bn) {
-    double best_cost = 0;
-    for (int64_t Vs = ti.logit_bm; Vs <= Vfull; Vs += ti.logit_bm) {
-      const int64_t slabs = cdiv(V, Vs);
-      const uint64_t need = (uint64_t)(B * Vs * esz) + (slabs > 1 ? (uint64_t)(B * d * 4) : 0) +
-                            bwd_tail(T, B, d, esz).bytes;
-      if (need > cap) break;  // need grows with Vs
-      const double c = backward_cost(T > 0 ? T : 1, d, V, B, Vs, ti);
-      if (best_B == 0 || c < best_cost * (1 - 1e-9)) {
-        best_cost = c;
-        best_B = B;
-        best_Vs = Vs;
-        best_slabs = slabs;
+  uint64_t best_split = 0;
+  for (int pass = 0; pass < 2 && best_B == 0; ++pass) {
+    for (int64_t B = (Tr < kMaxBlock ? Tr : kMaxBlock); B >= ti.logit_bn && best_B == 0;
+         B -= ti.logit_bn) {
+      const uint64_t reserve =
+          pass == 0 && 2 * cdiv(B, ti.dh_bm) * dh_nt <= flce::dh_split_slots() ? split : 0;
+      double best_cost = 0;
+      for (int64_t Vs = ti.logit_bm; Vs <= Vfull; Vs += ti.logit_bm) {
+        const int64_t slabs = cdiv(V, Vs);
+        const uint64_t need = (uint64_t)(B * Vs * esz) +
+                              (slabs > 1 ? (uint64_t)(B * d * 4) : 0) +
+                              bwd_tail(T, B, d, esz).bytes + reserve;
+        if (need > cap) break;  // need grows with Vs
+        const double c = backward_cost(T > 0 ? T : 1, d, V, B, Vs, ti);
+        if (best_B == 0 || c < best_cost * (1 - 1e-9)) {
+          best_cost = c;
+          best_B = B;
+          best_Vs = Vs;
+          best_slabs = slabs;
+          best_split = reserve;
+        }
       }
     }
   }
@@ -551,7 +575,12 @@ flce_status_t flce_plan(int64_t T, int64_t d, int64_t V, flce_dtype_t dtype, uin
   p.n_slabs = best_slabs;
   p.dz_ws_bytes = (uint64_t)(best_B * best_Vs * esz);
   p.dh_acc_bytes = best_slabs > 1 ? (uint64_t)(best_B * d * 4) : 0;
-  p.bwd_ws_bytes = p.dz_ws_bytes + p.dh_acc_bytes + bwd_tail(T, best_B, d, esz).bytes;
+  const uint64_t bwd_base = p.dz_ws_bytes + p.dh_acc_bytes + bwd_tail(T, best_B, d, esz).bytes;
+  // Without a planned split, the partial tiles still help blocks that
+  // ignored tokens thin out; they are kept where they fit beside the chosen
+  // block and slab.
+  p.dh_split_bytes = best_split ? best_split : (bwd_base + split <= cap ? split : 0);
+  p.bwd_ws_bytes = bwd_base + p.dh_split_bytes;
   p.ws_bytes = (p.fwd_ws_bytes > p.bwd_ws_bytes ? p.fwd_ws_bytes : p.bwd_ws_bytes) + kScalarBytes;
   p.vocab_ws_cap = cap;
   p.naive_logits_bytes = (uint64_t)T * (uint64_t)V * (uint64_t)esz;

@@ -580,36 +580,40 @@ __global__ void __launch_bounds__(LogitCfg<E>::T::NT, 1) bwd_dz_kernel(DzArgs a)
 // 2 = last of several (acc + partial -> dH in E), 3 = only slab (-> dH in E).
 // (The K loop over a whole slab is long, so the epilogue's read of the
 // partial costs little here; dW, with a short K loop, preloads instead.)
-template <typename E>
-__global__ void __launch_bounds__(DhCfg<E>::T::NT, 1) bwd_dh_kernel(DhArgs a) {
-  using TL = typename DhCfg<E>::T;
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  constexpr int ESZ = TL::ESZ;
-  int tm, tn;
-  if (!xcd_tile(blockIdx.x, a.n_mtiles, a.n_ntiles, 4, tm, tn)) return;
+//
+// The tile grid is (block tokens / BM) x (d / BN): 256 tiles for 8,192 tokens
+// at d = 2,048, but fewer for smaller blocks, smaller d, or a block thinned
+// by ignored tokens, which would leave compute units idle for the whole long
+// K loop.  With a partial buffer (a.part) the kernel then cuts the slab's K
+// range into S = kDhSplitSlots / tiles contiguous parts (whole k stages), one
+// workgroup each, and stores each part's fp32 tile; bwd_dh_reduce_kernel sums
+// the S parts in ascending order and applies the mode.  S is computed on the
+// device from the block's token count, identically in both kernels.
+constexpr int kDhSplitSlots = 256;  // partial tiles the buffer holds; also the CU count
+
+template <typename TL>
+__device__ __forceinline__ int dh_splits(const DhArgs& a, int act_m) {
+  if (!a.part) return 1;
+  const int tiles = act_m * a.n_ntiles;
+  if (tiles <= 0) return 1;
+  const int stages = (a.k_count + TL::BK - 1) / TL::BK;  // each part keeps at least one
+  return max(1, min(kDhSplitSlots / tiles, stages));
+}
+
+// Part `sp` of S of the tile (tm, tn), as stored by the dH kernel: register r
+// of block (i, j) of thread x at ((i * NI + j) * 16 + r) * NT + x, so that
+// every store and load of a register is NT consecutive floats.
+template <typename TL>
+__device__ __forceinline__ float* dh_part(const DhArgs& a, int act_m, int sp, int tm, int tn) {
+  return a.part + ((int64_t)(sp * act_m + tm) * a.n_ntiles + tn) * (TL::BM * TL::BN);
+}
+
+// The mode epilogue of one finished tile (rows tl0.., hidden columns n0..).
+template <typename E, typename TL>
+__device__ __forceinline__ void dh_store(const DhArgs& a, const TL& tile, int64_t tl0, int64_t n0,
+                                         int t_count) {
   const int wave = threadIdx.x >> 6;
   const int wm = wave / TL::WN, wn = wave % TL::WN;
-  const int64_t tl0 = (int64_t)tm * TL::BM;  // token within block
-  const int64_t n0 = (int64_t)tn * TL::BN;   // hidden index
-  const int t_count = block_count(a.blk);
-  if (tl0 >= t_count) return;
-
-  Operand A, B;
-  A.rs = make_rsrc(a.dz, clamp_bytes((int64_t)t_count * a.ldz * ESZ));
-  A.off = (uint32_t)(tl0 * a.ldz * ESZ);
-  A.ld_bytes = (uint32_t)(a.ldz * ESZ);
-  A.rows = (int)min<int64_t>(TL::BM, t_count - tl0);
-  A.cols = a.k_count;
-  B.rs = make_rsrc(a.W, clamp_bytes((int64_t)a.V * a.d * ESZ));
-  B.off = (uint32_t)((a.v_begin * a.d + n0) * ESZ);
-  B.ld_bytes = (uint32_t)(a.d * ESZ);
-  B.rows = a.k_count;
-  B.cols = (int)min<int64_t>(TL::BN, a.d - n0);
-
-  TL tile;
-  tile.zero();
-  tile.mainloop(A, B, a.k_count, lds);
-
 #pragma unroll
   for (int j = 0; j < TL::NI; ++j) {
     const int64_t n = n0 + TL::col_of(wn, j);
@@ -631,6 +635,106 @@ __global__ void __launch_bounds__(DhCfg<E>::T::NT, 1) bwd_dh_kernel(DhArgs a) {
           *out = (E)v;
         }
       }
+  }
+}
+
+template <typename E>
+__global__ void __launch_bounds__(DhCfg<E>::T::NT, 1) bwd_dh_kernel(DhArgs a) {
+  using TL = typename DhCfg<E>::T;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  constexpr int ESZ = TL::ESZ;
+  const int t_count = block_count(a.blk);
+  const int act_m = (t_count + TL::BM - 1) / TL::BM;
+  const int S = dh_splits<TL>(a, act_m);
+  // split-major virtual token tiles: the workgroups an XCD runs together
+  // share one part's W panels
+  int tv, tn;
+  if (!xcd_tile(blockIdx.x, act_m * S, a.n_ntiles, 4, tv, tn)) return;
+  const int sp = tv / act_m, tm = tv % act_m;
+  const int64_t tl0 = (int64_t)tm * TL::BM;  // token within block
+  const int64_t n0 = (int64_t)tn * TL::BN;   // hidden index
+  const int stages = (a.k_count + TL::BK - 1) / TL::BK;
+  const int k_lo = (int)((int64_t)stages * sp / S) * TL::BK;
+  const int k_hi = min(a.k_count, (int)((int64_t)stages * (sp + 1) / S) * TL::BK);
+  const int K = k_hi - k_lo;  // >= 1: S <= stages
+
+  Operand A, B;
+  A.rs = make_rsrc(a.dz, clamp_bytes((int64_t)t_count * a.ldz * ESZ));
+  A.off = (uint32_t)((tl0 * a.ldz + k_lo) * ESZ);
+  A.ld_bytes = (uint32_t)(a.ldz * ESZ);
+  A.rows = (int)min<int64_t>(TL::BM, t_count - tl0);
+  A.cols = K;
+  B.rs = make_rsrc(a.W, clamp_bytes((int64_t)a.V * a.d * ESZ));
+  B.off = (uint32_t)(((a.v_begin + k_lo) * a.d + n0) * ESZ);
+  B.ld_bytes = (uint32_t)(a.d * ESZ);
+  B.rows = K;
+  B.cols = (int)min<int64_t>(TL::BN, a.d - n0);
+
+  TL tile;
+  tile.zero();
+  __builtin_assume(K > 0);
+  tile.mainloop(A, B, K, lds);
+
+  if (S == 1) {
+    dh_store<E>(a, tile, tl0, n0, t_count);
+    return;
+  }
+  float* pt = dh_part<TL>(a, act_m, sp, tm, tn);
+#pragma unroll
+  for (int i = 0; i < TL::MI; ++i)
+#pragma unroll
+    for (int j = 0; j < TL::NI; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        pt[((i * TL::NI + j) * 16 + r) * TL::NT + threadIdx.x] = tile.acc[i][j][r];
+}
+
+// Sum of a split dH's parts in ascending part order, then the mode epilogue,
+// as an elementwise pass: each thread takes four consecutive floats of a
+// partial tile's register-major layout, which are four consecutive hidden
+// columns of one token row (lanes 4c..4c+3 of one register), so partials are
+// read as 16-byte vectors and the accumulator / dH rows are accessed four
+// columns at a time.  Nothing to do when the dH kernel ran unsplit (S = 1).
+template <typename E>
+__global__ void __launch_bounds__(256) bwd_dh_reduce_kernel(DhArgs a) {
+  using TL = typename DhCfg<E>::T;
+  const int t_count = block_count(a.blk);
+  const int act_m = (t_count + TL::BM - 1) / TL::BM;
+  const int S = dh_splits<TL>(a, act_m);
+  if (S == 1) return;
+  constexpr int kQuads = TL::BM * TL::BN / 4;  // 4-float groups per tile
+  const int64_t n_units = (int64_t)act_m * a.n_ntiles * kQuads;
+  for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < n_units;
+       u += (int64_t)gridDim.x * 256) {
+    const int tile = (int)(u / kQuads);
+    const int e = (int)(u % kQuads) * 4;  // element in the register-major tile
+    const int tm = tile / a.n_ntiles, tn = tile % a.n_ntiles;
+    f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < S; ++sp)
+      v += *reinterpret_cast<const f32x4_t*>(dh_part<TL>(a, act_m, sp, tm, tn) + e);
+    // element e = (register reg, thread x): reg = (i * NI + j) * 16 + r
+    const int reg = e / TL::NT, x = e % TL::NT;
+    const int r = reg % 16, ij = reg / 16, i = ij / TL::NI, j = ij % TL::NI;
+    const int wave = x / 64, lane = x % 64;
+    const int wm = wave / TL::WN, wn = wave % TL::WN;
+    const int64_t tl = (int64_t)tm * TL::BM + wm * TL::WTM + i * 32 + 8 * (r >> 2) +
+                       4 * (lane >> 5) + (r & 3);
+    const int64_t n = (int64_t)tn * TL::BN + wn * TL::WTN + j * 32 + (lane & 31);
+    // d is a multiple of 8 and n of 4: the four columns are all in range or none
+    if (tl >= t_count || n >= a.d) continue;
+    f32x4_t* accp = reinterpret_cast<f32x4_t*>(a.dh_acc + tl * a.d + n);
+    if (a.mode == 1 || a.mode == 2) v += *accp;
+    if (a.mode == 0 || a.mode == 1) {
+      *accp = v;
+    } else {
+      const int64_t t = a.blk.idx[a.blk.t_begin + tl];
+      E* out = reinterpret_cast<E*>(a.dH) + t * a.d + n;
+      if constexpr (sizeof(E) == 2) {
+        *reinterpret_cast<bf16x4_t*>(out) = bf16x4_t{(E)v[0], (E)v[1], (E)v[2], (E)v[3]};
+      } else {
+        *reinterpret_cast<f32x4_t*>(out) = v;
+      }
+    }
   }
 }
 
@@ -1008,19 +1112,38 @@ hipError_t launch_bwd_dz(const DzArgs& a, bool bf16, hipStream_t s) {
   return launch(bwd_dz_kernel<float>, grid, TL::NT, TL::LDS_BYTES, s, a);
 }
 
-hipError_t launch_bwd_dh(const DhArgs& a, bool bf16, hipStream_t s) {
-  const int grid = xcd_grid(a.n_mtiles, a.n_ntiles);
-  if (bf16) {
-    using TL = DhCfg<__bf16>::T;
-    hipError_t e = set_lds(bwd_dh_kernel<__bf16>, TL::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    return launch(bwd_dh_kernel<__bf16>, grid, TL::NT, TL::LDS_BYTES, s, a);
-  }
-  using TL = DhCfg<float>::T;
-  hipError_t e = set_lds(bwd_dh_kernel<float>, TL::LDS_BYTES);
+template <typename E>
+static hipError_t launch_dh(const DhArgs& a, hipStream_t s) {
+  using TL = typename DhCfg<E>::T;
+  // unsplit: every tile of the full block; split: at most kDhSplitSlots
+  // (part, tile) pairs, whatever the device's token count
+  int tiles = a.n_mtiles * a.n_ntiles;
+  if (a.part && tiles < kDhSplitSlots) tiles = kDhSplitSlots;
+  hipError_t e = set_lds(bwd_dh_kernel<E>, TL::LDS_BYTES);
   if (e != hipSuccess) return e;
-  return launch(bwd_dh_kernel<float>, grid, TL::NT, TL::LDS_BYTES, s, a);
+  return launch(bwd_dh_kernel<E>, xcd_grid(tiles, 1), TL::NT, TL::LDS_BYTES, s, a);
 }
+
+hipError_t launch_bwd_dh(const DhArgs& a, bool bf16, hipStream_t s) {
+  return bf16 ? launch_dh<__bf16>(a, s) : launch_dh<float>(a, s);
+}
+
+template <typename E>
+static hipError_t launch_dh_reduce(const DhArgs& a, hipStream_t s) {
+  using TL = typename DhCfg<E>::T;
+  // grid-stride over the full block's tiles (the device's count is smaller
+  // or equal); 8 workgroups of 256 threads per compute unit at most
+  const int64_t units = (int64_t)a.n_mtiles * a.n_ntiles * (TL::BM * TL::BN / 4);
+  const int64_t blocks = (units + 255) / 256;
+  return launch(bwd_dh_reduce_kernel<E>, (int)(blocks < 2048 ? blocks : 2048), 256, 0, s, a);
+}
+
+hipError_t launch_bwd_dh_reduce(const DhArgs& a, bool bf16, hipStream_t s) {
+  if (!a.part) return hipSuccess;
+  return bf16 ? launch_dh_reduce<__bf16>(a, s) : launch_dh_reduce<float>(a, s);
+}
+
+int dh_split_slots() { return kDhSplitSlots; }
 
 hipError_t launch_bwd_dw(const DwArgs& a, bool bf16, hipStream_t s) {
   const int grid = xcd_grid(a.n_mtiles, a.n_ntiles);

@@ -94,6 +94,9 @@ struct DhArgs {
   int mode;     // 0 first of several, 1 middle, 2 last of several, 3 only
   float* dh_acc;
   void* dH;
+  // fp32 partial tiles of a K-split dH, dh_split_slots() tiles of dh_bm x
+  // dh_bn; NULL: never split
+  float* part;
 };
 
 struct DwArgs {
@@ -133,6 +136,10 @@ hipError_t launch_loss_reduce(const ReduceArgs& a, hipStream_t s);
 hipError_t launch_cast_bf16(const float* src, void* dst, int64_t n, hipStream_t s);
 hipError_t launch_bwd_dz(const DzArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_dh(const DhArgs& a, bool bf16, hipStream_t s);
+// Sums a split dH's parts and applies the mode (nothing when unsplit); launch
+// after launch_bwd_dh with the same arguments.
+hipError_t launch_bwd_dh_reduce(const DhArgs& a, bool bf16, hipStream_t s);
+int dh_split_slots();
 hipError_t launch_bwd_dw(const DwArgs& a, bool bf16, hipStream_t s);
 // Scoring of given tokens: out[t * K + k] = H[t] . W[tokens[t * K + k]] - lse[t]
 // (lse NULL: the logit itself).

@@ -644,12 +644,16 @@ __device__ __forceinline__ void raster(int id, int nm, int nn, int group, int& t
 // (consecutive workgroup ids are dealt round-robin over the 8 XCDs, each with
 // its own L2) on a compact block of tiles: XCD x takes a contiguous range of
 // tile ids, rastered as above, so the ~32 workgroups an XCD runs at once
-// share a few A and B panels in its L2.  Returns false for the few padding
-// workgroups past the last tile.
+// share a few A and B panels in its L2.  Returns false for the padding
+// workgroups past the last tile, and for every workgroup beyond the first
+// xcd_grid(nm, nn) when the grid is larger (a tile count known only on the
+// device), whose ids would otherwise alias the next XCD's range.
 __device__ __forceinline__ bool xcd_tile(int bid, int nm, int nn, int group, int& tm, int& tn) {
   const int total = nm * nn;
   const int per = (total + 7) / 8;
-  const int id = (bid & 7) * per + (bid >> 3);
+  const int q = bid >> 3;
+  if (q >= per) return false;
+  const int id = (bid & 7) * per + q;
   if (id >= total) return false;
   raster(id, nm, nn, group, tm, tn);
   return true;

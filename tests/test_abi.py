@@ -45,9 +45,22 @@ def test_library_exports_every_declared_symbol(lib):
         assert getattr(lib, name) is not None
 
 
-def test_plan_struct_size_matches_header(lib):
-    # 3 int64 + 6 int32 + 4 int64 + 7 uint64 + 2 uint32
-    assert ctypes.sizeof(flce.Plan) == 3 * 8 + 6 * 4 + 4 * 8 + 7 * 8 + 2 * 4
+def test_plan_struct_layout_matches_header(tmp_path):
+    """The ctypes mirror of flce_plan_t has the C compiler's size and field
+    offsets (include/flce.h built as plain C99)."""
+    fields = [f for f, _ in flce.Plan._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stddef.h>\n#include <stdio.h>\n#include \"flce.h\"\n"
+                   "int main(void) {\n  printf(\"%zu\\n\", sizeof(flce_plan_t));\n" +
+                   "".join(f"  printf(\"%zu\\n\", offsetof(flce_plan_t, {f}));\n" for f in fields) +
+                   "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(exe)], check=True)
+    out = [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    assert out[0] == ctypes.sizeof(flce.Plan)
+    assert out[1:] == [getattr(flce.Plan, f).offset for f in fields]
 
 
 def test_version_and_status_strings(lib):

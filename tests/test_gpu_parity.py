@@ -185,6 +185,46 @@ def test_ignored_tokens_across_blocks(pattern, dtype):
 
 
 @pytest.mark.parametrize("dtype", [wl.DTYPE_F32, wl.DTYPE_BF16])
+def test_split_dH_over_slabs(dtype):
+    """dH of a 600-token block has 3 (bf16) or 5 (fp32) tiles at d = 64, so
+    the planner reserves partial tiles and the device cuts each slab's K loop
+    into many parts; the cap forces several vocab slabs, so the parts' sum
+    passes through the first / middle / last accumulator modes."""
+    T, d, V = 600, 64, 150000
+    inp = wl.make_inputs(T, d, V, dtype, seed=29, sigma_w=0.4, ignore_frac=0.1)
+    cap = 124_000_000 if dtype == wl.DTYPE_BF16 else 116_000_000
+    got = run_gpu(inp, grad_scale=0.5, cap=cap)
+    plan = got["plan"]
+    log("plan", plan.n_blocks, plan.n_slabs, plan.bwd_block, plan.bwd_slab, plan.dh_split_bytes)
+    assert plan.n_slabs >= 3 and plan.dh_split_bytes > 0
+    compare(got, _ref(inp, 0.5), dtype)
+
+
+@pytest.mark.parametrize("dtype", [wl.DTYPE_F32, wl.DTYPE_BF16])
+@pytest.mark.parametrize("pattern", ["suffix", "prefix", "alternate"])
+def test_split_dH_thinned_blocks(pattern, dtype):
+    """Token blocks of 8,192 with split dH, thinned by ignored tokens: the
+    device picks each block's split from its token count (full blocks, a
+    half-full one, an empty one), and dH rows land at the tokens' own rows."""
+    T, d, V = 20000, 64, 900
+    inp = wl.make_inputs(T, d, V, dtype, seed=43, sigma_w=0.4)
+    if pattern == "suffix":
+        inp.y[12000:] = IGN
+    elif pattern == "prefix":
+        inp.y[:15000] = IGN
+    else:
+        inp.y[::2] = IGN
+    base = np.random.default_rng(5).standard_normal((V, d)).astype(np.float32)
+    got = run_gpu(inp, grad_scale=0.5, accumulate_dW=True, dW_init=base)
+    plan = got["plan"]
+    assert plan.n_blocks >= 3 and plan.dh_split_bytes > 0
+    ref = _ref(inp, 0.5)
+    ref["dW"] = ref["dW"] + base
+    compare(got, ref, dtype)
+    assert np.all(got["dH"][inp.y == IGN] == 0.0)
+
+
+@pytest.mark.parametrize("dtype", [wl.DTYPE_F32, wl.DTYPE_BF16])
 def test_accumulate_dW(dtype):
     inp = wl.make_inputs(300, 48, 700, dtype, seed=19, sigma_w=0.4)
     base = np.random.default_rng(0).standard_normal((700, 48)).astype(np.float32)
