@@ -93,6 +93,28 @@ def test_plan_accepts_dW_beyond_2GiB(lib):
     assert 152064 * 3584 * 4 > 2 ** 31
 
 
+def test_plan_dH_split_policy(lib):
+    split = 256 * 256 * 256 * 4  # 256 partial tiles of 256 x 256 fp32
+    # the pages' shape: 902 MB without the buffer, no room for it under the cap
+    p = flce.flce_plan(65536, 2048, 124160, flce.FLCE_BF16)
+    assert p.dh_split_bytes == 0 and (p.bwd_block, p.bwd_slab) == (8192, 46848)
+    # 4,096 tokens at d = 2,048: 128 dH tiles, the buffer is planned
+    p = flce.flce_plan(4096, 2048, 32000, flce.FLCE_BF16)
+    assert p.dh_split_bytes == split
+    assert p.bwd_ws_bytes == (p.dz_ws_bytes + p.dh_acc_bytes + 2 * p.bwd_block * 2048 * 2 +
+                              4096 * 4 + 256 + 256 + split)
+    # a cap too small for the buffer: planned without it
+    cap = 512 * (96 * 4 + 256 * 2)
+    p = flce.flce_plan(1100, 96, 3000, flce.FLCE_BF16, cap)
+    assert p.dh_split_bytes == 0 and p.bwd_ws_bytes <= cap
+    # planned inside the cap, before the slab: several slabs and the buffer
+    p = flce.flce_plan(600, 64, 150000, flce.FLCE_BF16, 124_000_000)
+    assert p.dh_split_bytes == split and p.n_slabs >= 3 and p.bwd_ws_bytes <= 124_000_000
+    # fp32 tiles are 128 x 128
+    p = flce.flce_plan(256, 128, 1000, flce.FLCE_F32)
+    assert p.dh_split_bytes == 256 * 128 * 128 * 4
+
+
 def test_plan_null_out(lib):
     assert lib.flce_plan(10, 128, 1000, 1, 0, None) == flce.FLCE_ERR_INVALID_ARG
 
