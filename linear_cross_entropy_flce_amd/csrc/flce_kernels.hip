@@ -970,28 +970,58 @@ __device__ __forceinline__ float dot16(const u32x4_t& h, const u32x4_t& w, float
   return acc;
 }
 
+// N gathered rows of one position at once: the loads of all N rows' chunks
+// and of the position's H chunk are issued together, so a wave keeps
+// (N + 1) x 16 bytes per lane per chunk step in flight instead of walking
+// the rows one after another.  Each (lane, row) accumulates its chunks in
+// ascending order, as for a single row; rows past `nk` or with an id outside
+// the vocabulary read H's row instead and are not written.
+template <typename E, int N>
+__device__ __forceinline__ void token_logit_rows(const TokenArgs& a, int64_t t, int k0, int nk,
+                                                 const char* h, float lse, int lane) {
+  constexpr int CW = 16 / (int)sizeof(E);
+  const int nc = a.d / CW;
+  const char* w[N];
+  bool ok[N];
+#pragma unroll
+  for (int r = 0; r < N; ++r) {
+    const int64_t v = r < nk ? a.tokens[t * a.K + k0 + r] : -1;
+    ok[r] = v >= 0 && v < a.V;
+    w[r] = ok[r] ? reinterpret_cast<const char*>(a.W) + v * a.d * (int64_t)sizeof(E) : h;
+  }
+  float acc[N];
+#pragma unroll
+  for (int r = 0; r < N; ++r) acc[r] = 0.f;
+#pragma unroll 4
+  for (int c = lane; c < nc; c += 64) {
+    const u32x4_t hv = *reinterpret_cast<const u32x4_t*>(h + (int64_t)c * 16);
+    u32x4_t wv[N];
+#pragma unroll
+    for (int r = 0; r < N; ++r) wv[r] = *reinterpret_cast<const u32x4_t*>(w[r] + (int64_t)c * 16);
+#pragma unroll
+    for (int r = 0; r < N; ++r) acc[r] = dot16(hv, wv[r], acc[r], (E*)nullptr);
+  }
+#pragma unroll
+  for (int r = 0; r < N; ++r) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) acc[r] += __shfl_xor(acc[r], o);
+    if (lane == 0 && r < nk) a.out[t * a.K + k0 + r] = ok[r] ? acc[r] - lse : __builtin_nanf("");
+  }
+}
+
 template <typename E>
 __global__ void __launch_bounds__(256) token_logit_kernel(TokenArgs a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + wave;
   if (t >= a.T) return;
-  constexpr int CW = 16 / (int)sizeof(E);
-  const int nc = a.d / CW;
   const char* h = reinterpret_cast<const char*>(a.H) + t * a.d * (int64_t)sizeof(E);
   const float lse = a.lse ? a.lse[t] : 0.f;
-  for (int k = 0; k < a.K; ++k) {
-    const int64_t v = a.tokens[t * a.K + k];
-    const bool ok = v >= 0 && v < a.V;
-    float acc = 0.f;
-    if (ok) {
-      const char* w = reinterpret_cast<const char*>(a.W) + v * a.d * (int64_t)sizeof(E);
-      for (int c = lane; c < nc; c += 64)
-        acc = dot16(*reinterpret_cast<const u32x4_t*>(h + (int64_t)c * 16),
-                    *reinterpret_cast<const u32x4_t*>(w + (int64_t)c * 16), acc, (E*)nullptr);
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-    if (lane == 0) a.out[t * a.K + k] = ok ? acc - lse : __builtin_nanf("");
+  for (int k0 = 0; k0 < a.K; k0 += 8) {
+    const int nk = min(8, a.K - k0);
+    if (nk == 1) token_logit_rows<E, 1>(a, t, k0, nk, h, lse, lane);
+    else if (nk == 2) token_logit_rows<E, 2>(a, t, k0, nk, h, lse, lane);
+    else if (nk <= 4) token_logit_rows<E, 4>(a, t, k0, nk, h, lse, lane);
+    else token_logit_rows<E, 8>(a, t, k0, nk, h, lse, lane);
   }
 }
 
