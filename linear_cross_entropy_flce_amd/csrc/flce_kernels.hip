@@ -21,9 +21,13 @@
 //   gather_block one token block of H in that order, as rows and transposed.
 //   bwd_dz       recomputed logits tile -> dZ = g * (exp(z - lse) - onehot),
 //                stored (bf16 or fp32) to the [block x slab] workspace.
-//   bwd_dh       dH_block (+)= dZ W_slab   (fp32 accumulate, cast at the end).
+//   bwd_dh       dH_block (+)= dZ W_slab   (fp32 accumulate, cast at the end);
+//                cuts the slab's K loop into parts when the block has too few
+//                tiles to occupy the GPU.
+//   bwd_dh_reduce  sums those parts in order and applies the accumulator mode.
 //   bwd_dw       dW_slab^T (+)= H_block^T dZ (fp32, deterministic block order).
-//   token_logit  gathered h . w minus lse for given tokens (scoring).
+//   token_logit  gathered h . w minus lse for given tokens (scoring), up to
+//                eight gathered rows per pass.
 //   cast_bf16    optional bf16 copy of dW.
 #include <hip/hip_runtime.h>
 
