@@ -97,8 +97,10 @@ hipEvent_t pooled_event(Timing& t) {
     t.pool.pop_back();
     return e;
   }
+  // timing only: no system-scope fence at record (no cache writeback and
+  // invalidate between the launches being timed)
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 
