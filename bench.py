@@ -71,11 +71,13 @@ def cpu_baseline(inp, cfg, n_rows: int):
             "seconds": dt, "host_cpus": os.cpu_count()}
 
 
-def measured_traffic(kernel: str, workload: str):
+def measured_traffic(kernel: str, workload: str, plan_key: dict):
     """HBM bytes per launch of `kernel` from the committed profiler summary,
-    or None when there is none for this workload or the kernel sources have
-    changed since the counters were taken."""
+    or None when there is none for this workload, or when the library's
+    device code or the workload's plan (its launch shapes) differ from those
+    the counters were taken with."""
     import glob
+    code = device_code_digest()
     for path in glob.glob(os.path.join(ROOT, "profiles", "traffic_*.json")):
         try:
             rec = json.load(open(path))
@@ -83,56 +85,58 @@ def measured_traffic(kernel: str, workload: str):
             continue
         if not rec.get("workload", "").startswith(workload):
             continue
-        try:
-            digest = code_digest(rec.get("source_files", []))
-        except OSError:
-            return None
-        if digest != rec.get("source_sha256"):
+        if code is None or rec.get("device_code_sha256") != code or rec.get("plan") != plan_key:
             return None
         k = rec.get("per_launch", {}).get(kernel)
         return None if k is None else int(k["traffic_bytes"])
     return None
 
 
-def code_digest(files) -> str:
-    """SHA-256 of the C/C++ sources with comments removed and whitespace runs
-    collapsed, so that the recorded traffic survives edits that leave the
-    compiled code as it was."""
+def elf_section(path: str, name: str):
+    """Bytes of the named section of a 64-bit little-endian ELF file, or None."""
+    import struct
+    data = open(path, "rb").read()
+    if data[:4] != b"\x7fELF" or data[4] != 2 or data[5] != 1:
+        return None
+    shoff, = struct.unpack_from("<Q", data, 0x28)
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", data, 0x3A)
+
+    def header(i):  # (name, type, flags, addr, offset, size, ...)
+        return struct.unpack_from("<IIQQQQIIQQ", data, shoff + i * shentsize)
+
+    names = header(shstrndx)[4]
+    for i in range(shnum):
+        h = header(i)
+        start = names + h[0]
+        if data[start:data.index(b"\0", start)].decode() == name:
+            return data[h[4]:h[4] + h[5]]
+    return None
+
+
+def device_code_digest(lib_path: str = None):
+    """SHA-256 of the GPU code objects embedded in libflce.so (its
+    .hip_fatbin section): unchanged by host-only or comment edits, changed
+    by any edit that changes a kernel."""
     import hashlib
-    h = hashlib.sha256()
-    for f in files:
-        src = open(os.path.join(ROOT, f), encoding="utf-8").read()
-        out, i, n = [], 0, len(src)
-        while i < n:
-            c = src[i]
-            if c == "/" and src.startswith("//", i):
-                j = src.find("\n", i)
-                i = n if j < 0 else j
-            elif c == "/" and src.startswith("/*", i):
-                j = src.find("*/", i + 2)
-                i = n if j < 0 else j + 2
-                out.append(" ")
-            elif c in "\"'":
-                j = i + 1
-                while j < n and src[j] != c:
-                    j += 2 if src[j] == "\\" else 1
-                out.append(src[i:j + 1])
-                i = j + 1
-            else:
-                out.append(c)
-                i += 1
-        h.update(" ".join("".join(out).split()).encode())
-        h.update(b"\0")
-    return h.hexdigest()
+    if lib_path is None:
+        from linear_cross_entropy_flce_amd import _lib
+        lib_path = _lib.LIB_PATH
+    try:
+        code = elf_section(lib_path, ".hip_fatbin")
+    except OSError:
+        return None
+    return None if code is None else hashlib.sha256(code).hexdigest()
 
 
-TRAFFIC_SOURCES = ["linear_cross_entropy_flce_amd/csrc/flce_kernels.hip",
-                   "linear_cross_entropy_flce_amd/csrc/flce_tile.hpp",
-                   "linear_cross_entropy_flce_amd/csrc/flce_api.cpp"]
+def plan_key(plan) -> dict:
+    """The plan fields that shape the launches (grids, K loops, workspace)."""
+    return {f: int(getattr(plan, f)) for f in ("fwd_splits", "fwd_tiles_per_split", "bwd_block",
+                                                 "bwd_slab", "n_blocks", "n_slabs",
+                                                 "dh_split_bytes")}
 
 
 def summarize_traffic(fetch_csv: str, write_csv: str, cfetch_csv: str, cwrite_csv: str,
-                      workload: str) -> dict:
+                      workload: str, plan: dict) -> dict:
     """HBM bytes per launch of each library kernel from four rocprofv3
     counter-collection CSVs: FETCH_SIZE and WRITE_SIZE over bench steps, and
     the same two counters over --copy-calibration, whose copy kernel moves a
@@ -192,11 +196,12 @@ def summarize_traffic(fetch_csv: str, write_csv: str, cfetch_csv: str, cwrite_cs
     return {
         "about": "HBM traffic per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per "
                  "dispatch), each divided by the value the same counter reads per byte of a plain "
-                 "1 GiB device copy (bench.py --copy-calibration 1024). Valid only while the "
-                 "kernel sources, comments and whitespace aside, hash to source_sha256.",
+                 "1 GiB device copy (bench.py --copy-calibration 1024). Valid only while "
+                 "libflce.so's GPU code (.hip_fatbin) hashes to device_code_sha256 and the "
+                 "workload's plan is the one recorded.",
         "workload": workload,
-        "source_files": TRAFFIC_SOURCES,
-        "source_sha256": code_digest(TRAFFIC_SOURCES),
+        "device_code_sha256": device_code_digest(),
+        "plan": plan,
         "calibration": {"copy_bytes": cal_bytes,
                         "fetch_counter_bytes_per_byte": round(f_per_byte, 4),
                         "write_counter_bytes_per_byte": round(w_per_byte, 4)},
@@ -370,9 +375,13 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.traffic_summary:
+        import linear_cross_entropy_flce_amd as flce
         import workloads as wl
+        cfg = wl.CONFIGS[args.config]
         print(json.dumps(summarize_traffic(*args.traffic_summary,
-                                           workload=wl.CONFIGS[args.config].name + " (one bench step)"),
+                                           workload=cfg.name + " (one bench step)",
+                                           plan=plan_key(flce.flce_plan(cfg.T, cfg.d, cfg.V,
+                                                                        cfg.dtype))),
                          indent=1))
         return
 
@@ -470,7 +479,7 @@ def main():
     achieved = flops_per_launch / (avg_ms / 1e3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom_name, "achieved": round(achieved, 2),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": measured_traffic(dom_name, cfg.name), "flops_per_launch": flops_per_launch,
+                "traffic": measured_traffic(dom_name, cfg.name, plan_key(plan)), "flops_per_launch": flops_per_launch,
                 "avg_launch_ms": round(avg_ms, 4), "launches": dom["launches"]}
 
     shard = shard_leg(flce, wl, H, W, cfg, ws, stream, args.shard_steps) if args.shard_steps > 0 else None

@@ -9,6 +9,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -138,8 +139,10 @@ class Timed {
 // runs whole rounds of kComputeUnits workgroups, so a grid of n tiles costs
 // ceil(n / CU) rounds; the recompute tile also pays its exp/store epilogue,
 // the dW tile its fp32 read-modify-write, and each slab a dH accumulator pass.
+// With dh_split, a block of at most half a round of dH tiles runs its K loop
+// in S parts (the kernels' rule), one round of 1/S of the tile.
 double backward_cost(int64_t T, int64_t d, int64_t V, int64_t B, int64_t Vs,
-                     const flce::TileInfo& ti) {
+                     const flce::TileInfo& ti, bool dh_split) {
   const double unit = 256.0 * 256.0 * 256.0;
   const int64_t n_dt_h = cdiv(d, ti.dh_bn), n_dt_w = cdiv(d, ti.dw_bm);
   double cost = 0;
@@ -154,7 +157,11 @@ double backward_cost(int64_t T, int64_t d, int64_t V, int64_t B, int64_t Vs,
       const double dh_tile = (double)ti.dh_bm * ti.dh_bn * vc / unit;
       const double dw_tile = (double)ti.dw_bm * ti.dw_bn * tc / unit;
       cost += cdiv(dz_tiles, kComputeUnits) * dz_tile * 1.10;
-      cost += cdiv(dh_tiles, kComputeUnits) * (dh_tile + 0.5);
+      const int64_t dh_parts =
+          dh_split && 2 * dh_tiles <= kComputeUnits
+              ? std::min<int64_t>(kComputeUnits / dh_tiles, cdiv(vc, ti.dh_bk))
+              : 1;
+      cost += cdiv(dh_tiles, kComputeUnits) * (dh_tile / dh_parts + 0.5);
       cost += cdiv(dw_tiles, kComputeUnits) * dw_tile * (t0 > 0 ? 1.07 : 1.035);
     }
   }
@@ -556,7 +563,7 @@ flce_status_t flce_plan(int64_t T, int64_t d, int64_t V, flce_dtype_t dtype, uin
                               (slabs > 1 ? (uint64_t)(B * d * 4) : 0) +
                               bwd_tail(T, B, d, esz).bytes + reserve;
         if (need > cap) break;  // need grows with Vs
-        const double c = backward_cost(T > 0 ? T : 1, d, V, B, Vs, ti);
+        const double c = backward_cost(T > 0 ? T : 1, d, V, B, Vs, ti, reserve > 0);
         if (best_B == 0 || c < best_cost * (1 - 1e-9)) {
           best_cost = c;
           best_B = B;

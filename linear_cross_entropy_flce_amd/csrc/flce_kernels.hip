@@ -1211,6 +1211,7 @@ TileInfo tile_info(bool bf16) {
     t.dh_bn = DhCfg<__bf16>::T::BN;
     t.dw_bm = DwCfg<__bf16>::T::BM;
     t.dw_bn = DwCfg<__bf16>::T::BN;
+    t.dh_bk = DhCfg<__bf16>::T::BK;
   } else {
     t.logit_bm = LogitCfg<float>::T::BM;
     t.logit_bn = LogitCfg<float>::T::BN;
@@ -1218,6 +1219,7 @@ TileInfo tile_info(bool bf16) {
     t.dh_bn = DhCfg<float>::T::BN;
     t.dw_bm = DwCfg<float>::T::BM;
     t.dw_bn = DwCfg<float>::T::BN;
+    t.dh_bk = DhCfg<float>::T::BK;
   }
   return t;
 }

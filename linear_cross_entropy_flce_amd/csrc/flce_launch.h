@@ -116,6 +116,7 @@ struct DwArgs {
 struct TileInfo {
   // logits: vocab x tokens; dH: tokens x hidden; dW: hidden x vocab
   int logit_bm, logit_bn, dh_bm, dh_bn, dw_bm, dw_bn;
+  int dh_bk;  // k (vocab) per dH stage: the unit of its K split
 };
 
 TileInfo tile_info(bool bf16);

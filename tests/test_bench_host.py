@@ -1,8 +1,10 @@
-"""Host-side logic of bench.py (no GPU): the source digest that keeps the
-recorded HBM traffic tied to the code it was measured on, the conversion of
-profiler byte counters into per-launch bytes, and the one-GPU guard."""
+"""Host-side logic of bench.py (no GPU): the device-code digest and plan key
+that tie the recorded HBM traffic to the code and launch shapes it was
+measured with, the conversion of profiler byte counters into per-launch
+bytes, and the one-GPU guard."""
 import csv
 import importlib.util
+import json
 import os
 import subprocess
 import sys
@@ -20,37 +22,57 @@ def bench():
     return mod
 
 
-def _digest_of(bench, tmp_path, text):
-    (tmp_path / "k.hip").write_text(text)
-    old = bench.ROOT
-    bench.ROOT = str(tmp_path)
-    try:
-        return bench.code_digest(["k.hip"])
-    finally:
-        bench.ROOT = old
+@pytest.fixture(scope="module")
+def libpath():
+    from linear_cross_entropy_flce_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from linear_cross_entropy_flce_amd import build
+        build.build()
+    return _lib.LIB_PATH
 
 
-def test_digest_ignores_comments_and_layout(bench, tmp_path):
-    base = _digest_of(bench, tmp_path, 'int f(int x) {\n  return x + 1;  // add one\n}\n')
-    same = [
-        'int f(int x) { return x + 1; }\n',
-        '// header\nint f(int x) {\n\n    return x + 1;\n}\n',
-        'int f(int x) { /* multi\n line */ return x + 1; }\n',
-    ]
-    for text in same:
-        assert _digest_of(bench, tmp_path, text) == base, text
+def _section_span(bench, path, name):
+    data = open(path, "rb").read()
+    sec = bench.elf_section(path, name)
+    start = data.find(sec)
+    return data, start, len(sec)
 
 
-def test_digest_sees_code_and_string_changes(bench, tmp_path):
-    base = _digest_of(bench, tmp_path, 'int f(int x) { return x + 1; }\n')
-    assert _digest_of(bench, tmp_path, 'int f(int x) { return x + 2; }\n') != base
-    # comment markers inside a string are code, not comments
-    s1 = _digest_of(bench, tmp_path, 'const char* s = "a // b"; int g;\n')
-    s2 = _digest_of(bench, tmp_path, 'const char* s = "a // c"; int g;\n')
-    assert s1 != s2
-    e1 = _digest_of(bench, tmp_path, 'const char* s = "q\\" // x"; int g;\n')
-    e2 = _digest_of(bench, tmp_path, 'const char* s = "q\\" // y"; int g;\n')
-    assert e1 != e2
+def test_device_code_digest_covers_gpu_code_only(bench, libpath, tmp_path):
+    import hashlib
+    code = bench.elf_section(libpath, ".hip_fatbin")
+    assert code is not None and len(code) > 1024
+    assert bench.device_code_digest(libpath) == hashlib.sha256(code).hexdigest()
+    data, start, size = _section_span(bench, libpath, ".hip_fatbin")
+    # a byte of GPU code changed: another digest
+    gpu = bytearray(data)
+    gpu[start + size // 2] ^= 0xFF
+    (tmp_path / "gpu.so").write_bytes(bytes(gpu))
+    assert bench.device_code_digest(str(tmp_path / "gpu.so")) != bench.device_code_digest(libpath)
+    # a byte of host code changed: the same digest
+    text = bench.elf_section(libpath, ".text")
+    t0 = data.find(text)
+    host = bytearray(data)
+    host[t0 + len(text) // 2] ^= 0xFF
+    (tmp_path / "host.so").write_bytes(bytes(host))
+    assert bench.device_code_digest(str(tmp_path / "host.so")) == bench.device_code_digest(libpath)
+    assert bench.elf_section(str(tmp_path / "host.so"), ".no_such_section") is None
+
+
+def test_recorded_traffic_needs_same_code_and_plan(bench, libpath, tmp_path, monkeypatch):
+    plan = {"fwd_splits": 4, "bwd_block": 8192}
+    rec = {"workload": "wl_x (one bench step)", "device_code_sha256": bench.device_code_digest(),
+           "plan": plan, "per_launch": {"bwd_dw": {"traffic_bytes": 123}}}
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "profiles" / "traffic_x.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.measured_traffic("bwd_dw", "wl_x", plan) == 123
+    assert bench.measured_traffic("bwd_dz", "wl_x", plan) is None
+    assert bench.measured_traffic("bwd_dw", "wl_y", plan) is None
+    assert bench.measured_traffic("bwd_dw", "wl_x", dict(plan, bwd_block=4096)) is None
+    rec["device_code_sha256"] = "0" * 64
+    (tmp_path / "profiles" / "traffic_x.json").write_text(json.dumps(rec))
+    assert bench.measured_traffic("bwd_dw", "wl_x", plan) is None
 
 
 def _write_counter_csv(path, counter, rows):
@@ -63,7 +85,7 @@ def _write_counter_csv(path, counter, rows):
                         "Counter_Value": value})
 
 
-def test_traffic_summary_scales_by_copy_calibration(bench, tmp_path):
+def test_traffic_summary_scales_by_copy_calibration(bench, libpath, tmp_path):
     gib_kib = 1024 * 1024  # KiB in the 1 GiB calibration copy
     # the copy reads FETCH = 0.5 counted byte per byte and WRITE = 1.0
     _write_counter_csv(tmp_path / "cf.csv", "FETCH_SIZE",
@@ -77,7 +99,8 @@ def test_traffic_summary_scales_by_copy_calibration(bench, tmp_path):
                         (3, "unrelated_kernel", 5.0)])
     _write_counter_csv(tmp_path / "w.csv", "WRITE_SIZE", [(1, name, 64.0), (2, name, 128.0)])
     rec = bench.summarize_traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"),
-                                  str(tmp_path / "cf.csv"), str(tmp_path / "cw.csv"), "wl")
+                                  str(tmp_path / "cf.csv"), str(tmp_path / "cw.csv"), "wl",
+                                  {"bwd_block": 8192})
     assert rec["calibration"]["fetch_counter_bytes_per_byte"] == 0.5
     assert rec["calibration"]["write_counter_bytes_per_byte"] == 1.0
     k = rec["per_launch"]["bwd_dw"]
@@ -87,7 +110,8 @@ def test_traffic_summary_scales_by_copy_calibration(bench, tmp_path):
     assert k["write_bytes"] == 96 * 1024
     assert k["traffic_bytes"] == (600 + 96) * 1024
     assert "unrelated" not in rec["per_launch"]
-    assert rec["source_sha256"] == bench.code_digest(bench.TRAFFIC_SOURCES)
+    assert rec["device_code_sha256"] == bench.device_code_digest()
+    assert rec["plan"] == {"bwd_block": 8192}
 
 
 def test_more_than_one_gpu_is_refused():
