@@ -64,6 +64,39 @@ def test_unit_shapes(T, d, V, ign, dtype):
 
 
 @pytest.mark.parametrize("dtype", [wl.DTYPE_F32, wl.DTYPE_BF16])
+def test_empty_batch(dtype):
+    """T = 0: the reduced loss is 0, dW is zeroed (or left as it was when
+    accumulating), and the fused call does the same, for every dtype."""
+    import linear_cross_entropy_flce_amd as flce
+    d, V = 64, 1000
+    et = torch.float32 if dtype == wl.DTYPE_F32 else torch.bfloat16
+    dev = torch.device("cuda:0")
+    H = torch.empty((0, d), dtype=et, device=dev)
+    W = torch.randn((V, d), device=dev).to(et)
+    y = torch.empty(0, dtype=torch.int64, device=dev)
+    plan = flce.flce_plan(0, d, V, dtype)
+    ws = flce.workspace(plan, dev)
+    red = torch.full((1,), float("nan"), device=dev)
+    loss, lse, _ = flce.flce_forward(plan, H, W, y, IGN, 0.5, loss_reduced=red, ws=ws)
+    dW = torch.full((V, d), 7.0, device=dev)
+    dH, _ = flce.flce_backward(plan, H, W, y, lse, IGN, 1.0, dW=dW, ws=ws)
+    torch.cuda.synchronize()
+    assert loss.numel() == 0 and lse.numel() == 0 and dH.numel() == 0
+    assert red.item() == 0.0 and torch.count_nonzero(dW).item() == 0
+    dW.fill_(7.0)
+    flce.flce_backward(plan, H, W, y, lse, IGN, 1.0, dW=dW, accumulate_dW=True, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.all(dW == 7.0).item()
+    dW.fill_(7.0)
+    dWb = torch.full((V, d), 7.0, device=dev).to(torch.bfloat16)
+    out = flce.flce_forward_backward(plan, H, W, y, IGN, "mean_valid", 1.0, dW=dW, dW_bf16=dWb,
+                                     ws=ws)
+    torch.cuda.synchronize()
+    assert out["loss_reduced"].item() == 0.0
+    assert torch.count_nonzero(dW).item() == 0 and torch.count_nonzero(dWb).item() == 0
+
+
+@pytest.mark.parametrize("dtype", [wl.DTYPE_F32, wl.DTYPE_BF16])
 def test_targets_at_tile_edges(dtype):
     T, d, V = 64, 32, 1030
     inp = wl.make_inputs(T, d, V, dtype, seed=7, sigma_w=0.5)
@@ -124,10 +157,12 @@ def test_large_logits_running_max():
 
 
 @pytest.mark.parametrize("dtype", [wl.DTYPE_F32, wl.DTYPE_BF16])
-def test_long_hidden(dtype):
-    """d = 16,384 (a long K loop for the logit tiles, long rows for every
-    operand offset) with a ragged token count and vocabulary."""
-    T, d, V = 300, 16384, 700
+@pytest.mark.parametrize("d", [16384, 65536])
+def test_long_hidden(d, dtype):
+    """d = 16,384 and the largest supported d = 65,536 (long K loops for the
+    logit tiles, long rows for every operand offset, 256 hidden tiles in dH
+    and dW) with a ragged token count and vocabulary."""
+    T, V = 300, 700
     inp = wl.make_inputs(T, d, V, dtype, seed=37, sigma_w=0.02, ignore_frac=0.1)
     got = run_gpu(inp, grad_scale=0.5)
     # fp32: sums of 16,384 terms round by ~sqrt(d) ulps of |z|; the same
