@@ -11,9 +11,13 @@
 // (both KC), while dH = dZ W contracts W over the vocab axis and
 // dW = dZ^T H contracts H and dZ over the token axis (MC).
 //
-// Global -> LDS: direct DMA (buffer_load_dwordx4 ... lds), no register
-// staging, into a ring of NS stages that runs NS - 1 stages ahead of the MFMA
-// work (one barrier per stage).
+// Global -> LDS, three loaders (one barrier per stage each):
+//   - register-staged double buffer (DMA = false, NS = 2; what every kernel
+//     uses): buffer_load_dwordx4 into VGPRs 1.5 stages ahead, ds_write into
+//     the other LDS stage;
+//   - two-stage direct DMA (buffer_load_dwordx4 ... lds, no VGPR staging);
+//   - a DMA ring of NS > 2 stages running NS - 1 stages ahead.
+// LDS layouts, the same for all three:
 //   KC tiles are stored [row][KB bytes of k] with the 16-byte chunk index
 //   XOR-swizzled so that the lanes reading one MFMA fragment column hit
 //   distinct banks.
