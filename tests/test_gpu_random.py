@@ -1,4 +1,4 @@
-"""Seeded random shapes against the oracle.
+"""Seeded random shapes against the oracle, unsharded and as vocab shards.
 
 Each case draws its dtype, a ragged token count, hidden size and vocabulary,
 an ignored fraction, a weight scale, a gradient scale, sometimes a small
@@ -15,7 +15,7 @@ import torch
 import linear_cross_entropy_flce_amd as flce
 import oracle
 import workloads as wl
-from gpu_helpers import TOL, compare, log, logit_tol, run_gpu
+from gpu_helpers import TOL, compare, log, logit_tol, run_gpu, run_gpu_shards
 
 pytestmark = pytest.mark.gpu
 
@@ -92,4 +92,36 @@ def test_random_case(i):
     red = float(got["red"][0])
     ref_red = oracle.reduced_loss(loss, c["g"])
     assert abs(red - ref_red) <= ltol * max(1.0, c["g"] * c["T"]), (red, ref_red)
+    log("  errors", errs)
+
+
+N_SHARD_CASES = 24
+
+
+@pytest.mark.parametrize("i", range(N_SHARD_CASES))
+def test_random_shard_case(i):
+    """The vocab-parallel path over random shard cuts (2 to 4 shards, some
+    narrower than a vocab tile), merged in order, against the unsharded
+    oracle."""
+    rng = np.random.default_rng(7000 + i)
+    dtype = (wl.DTYPE_F32, wl.DTYPE_BF16)[i % 2]
+    T = int(rng.integers(1, 1500))
+    d = 8 * int(rng.integers(1, 49))
+    V = int(rng.integers(4, 12001))
+    n = int(rng.integers(2, 5))
+    cuts = np.sort(rng.choice(np.arange(1, V), size=min(n - 1, V - 1), replace=False))
+    bounds = [0, *[int(c) for c in cuts], V]
+    ign = float(rng.choice([0.0, 0.2, 0.9]))
+    targets = str(rng.choice(["uniform", "zipf"]))
+    g = float(rng.choice([1.0, 1.0 / T]))
+    log(f"shard case {i}: {dtype} T={T} d={d} V={V} bounds={bounds} ign={ign} {targets}")
+    inp = wl.make_inputs(T, d, V, dtype, seed=int(rng.integers(1 << 30)), sigma_w=0.3,
+                         targets=targets, ignore_frac=ign)
+    got = run_gpu_shards(inp, bounds, loss_scale=g, grad_scale=g)
+    Hf, Wf = inp.H_f32(), inp.W_f32()
+    loss, lse, dH, dW = oracle.forward_backward(Hf, Wf, inp.y, IGN, g)
+    zmax = float(np.abs(oracle.logits(Hf, Wf)).max())
+    ltol = logit_tol(dtype, d, zmax)
+    errs = compare(got, dict(loss=loss, lse=lse, dH=dH, dW=dW), dtype, loss_tol=ltol,
+                   grad_tol=TOL[dtype]["grad"] + (ltol - TOL[dtype]["loss"]))
     log("  errors", errs)
