@@ -58,6 +58,36 @@ def test_scores_match_oracle(T, d, V, K, dtype):
     assert max_abs(got[r, c], ref_logit - lse_ref[r]) <= tol
 
 
+@pytest.mark.parametrize("i", range(16))
+def test_random_scoring_case(i):
+    """Random T, d, V and K = 1..20 tokens per position (the kernel takes up
+    to eight gathered rows per pass, so K spans one to three passes and the
+    padded widths 1, 2, 4 and 8), with and without lse, some ids invalid."""
+    rng = np.random.default_rng(8000 + i)
+    dtype = (wl.DTYPE_F32, wl.DTYPE_BF16)[i % 2]
+    T = int(rng.integers(1, 800))
+    d = 8 * int(rng.integers(1, 129))
+    V = int(rng.integers(2, 9001))
+    K = int(rng.integers(1, 21))
+    log(f"scoring case {i}: {dtype} T={T} d={d} V={V} K={K}")
+    inp = wl.make_inputs(T, d, V, dtype, seed=int(rng.integers(1 << 30)), sigma_w=0.3)
+    H, W, y = device_inputs(inp)
+    tok = _tokens(int(rng.integers(1 << 30)), T, K, V, n_bad=min(6, T * K // 3))
+    plan = flce.flce_plan(T, d, V, dtype)
+    _, lse, _ = flce.flce_forward(plan, H, W, y, IGN)
+    tt = torch.from_numpy(tok).cuda()
+    got = flce.flce_token_logprobs(H, W, tt, lse).cpu().numpy()
+    raw = flce.flce_token_logprobs(H, W, tt).cpu().numpy()
+    Z = oracle.logits(inp.H_f32(), inp.W_f32())
+    lse_ref = oracle.log_sum_exp_rows(Z)
+    ok = (tok >= 0) & (tok < V)
+    assert np.all(np.isnan(got[~ok])) and np.all(np.isnan(raw[~ok]))
+    r, c = np.nonzero(ok)
+    tol = logit_tol(dtype, d, float(np.abs(Z).max()))
+    assert max_abs(raw[r, c], Z[r, tok[r, c]]) <= tol
+    assert max_abs(got[r, c], Z[r, tok[r, c]] - lse_ref[r]) <= tol
+
+
 @pytest.mark.parametrize("dtype", [wl.DTYPE_F32, wl.DTYPE_BF16])
 def test_target_scores_are_minus_loss(dtype):
     inp = wl.make_inputs(400, 128, 3000, dtype, seed=31, sigma_w=0.5, ignore_frac=0.2)
