@@ -72,6 +72,55 @@ def test_fused_equals_separate_and_oracle(T, d, V, ign, dtype):
     log("  mean_valid errors", errs)
 
 
+@pytest.mark.parametrize("i", range(12))
+def test_random_fused_case(i):
+    """Random shapes through the fused call: either reduction, sometimes
+    accumulating into an existing dW, sometimes with the bf16 copy; against
+    the oracle, and bit for bit against the separate calls with the same g."""
+    rng = np.random.default_rng(6000 + i)
+    dtype = (wl.DTYPE_F32, wl.DTYPE_BF16)[i % 2]
+    T = int(rng.integers(1, 2000))
+    d = 8 * int(rng.integers(1, 49))
+    V = int(rng.integers(2, 15001))
+    reduction = ("sum", "mean_valid")[int(rng.integers(2))]
+    scale = float(rng.choice([1.0, 0.5]))
+    acc = bool(rng.random() < 0.4)
+    with_bf16 = bool(rng.random() < 0.5)
+    ign = float(rng.choice([0.0, 0.3, 0.8]))
+    log(f"fused case {i}: {dtype} T={T} d={d} V={V} {reduction} scale={scale} acc={acc} "
+        f"bf16={with_bf16} ign={ign}")
+    inp = wl.make_inputs(T, d, V, dtype, seed=int(rng.integers(1 << 30)), sigma_w=0.3,
+                         ignore_frac=ign)
+    H, W, y = device_inputs(inp)
+    plan = flce.flce_plan(T, d, V, dtype)
+    n_valid = int((inp.y != IGN).sum())
+    g = scale if reduction == "sum" else (float(np.float32(scale) / np.float32(n_valid))
+                                          if n_valid else 0.0)
+    base = rng.standard_normal((V, d)).astype(np.float32)
+    dW = torch.from_numpy(base).cuda() if acc else None
+    dWb = torch.empty((V, d), dtype=torch.bfloat16, device=W.device) if with_bf16 else None
+    a = _fused(plan, H, W, y, reduction, scale, dW=dW, accumulate_dW=acc, dW_bf16=dWb)
+    # the separate calls with the same g
+    red = torch.empty(1, dtype=torch.float32, device=W.device)
+    loss, lse, _ = flce.flce_forward(plan, H, W, y, IGN, g, loss_reduced=red)
+    dW2 = torch.from_numpy(base).cuda() if acc else None
+    dH2, dW2 = flce.flce_backward(plan, H, W, y, lse, IGN, g, dW=dW2, accumulate_dW=acc)
+    torch.cuda.synchronize()
+    for k, v in (("loss", loss), ("lse", lse), ("dH", dH2), ("dW", dW2)):
+        assert np.array_equal(a[k], _np(v), equal_nan=True), k
+    if with_bf16:
+        assert np.array_equal(a["dW_bf16"], _np(dW2.to(torch.bfloat16)))
+    ref_loss, ref_lse, ref_dH, ref_dW = oracle.forward_backward(inp.H_f32(), inp.W_f32(), inp.y,
+                                                                IGN, g)
+    if acc:
+        ref_dW = ref_dW + base
+    tl = logit_tol(dtype, d, float(np.abs(oracle.logits(inp.H_f32(), inp.W_f32())).max()))
+    compare(a, dict(loss=ref_loss, lse=ref_lse, dH=ref_dH, dW=ref_dW), dtype, loss_tol=tl,
+            grad_tol=TOL[dtype]["grad"] + (tl - TOL[dtype]["loss"]))
+    ref_red = oracle.reduced_loss(ref_loss, g)
+    assert abs(float(a["loss_reduced"][0]) - ref_red) <= tl * max(1.0, g * T)
+
+
 def test_mean_over_no_tokens_is_zero():
     inp = wl.make_inputs(300, 64, 1000, wl.DTYPE_BF16, seed=5, sigma_w=0.5, ignore_frac=1.0)
     H, W, y = device_inputs(inp)
