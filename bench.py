@@ -41,6 +41,26 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def kernel_table(kernels: dict, steps: int, step_ms: float) -> dict:
+    """Per-kernel figures from the library's hipEvent timing: the contraction
+    kernels in TFLOP/s of their algorithmic flops, the memory-bound passes
+    (merges, reductions, casts, gathers) in GB/s of their algorithmic bytes
+    against the 8 TB/s HBM peak."""
+    out = {}
+    for k, v in kernels.items():
+        sec = v["total_ms"] / 1e3
+        e = {"launches": v["launches"], "avg_ms": round(v["total_ms"] / v["launches"], 4),
+             "share": round(v["total_ms"] / steps / step_ms, 4)}
+        if v["flops"]:
+            e["tflops"] = round(v["flops"] / sec / 1e12, 2) if sec else 0.0
+        else:
+            gbs = v["bytes"] / sec / 1e9 if sec else 0.0
+            e["gbs"] = round(gbs, 1)
+            e["hbm_frac"] = round(gbs / PEAK_HBM_GBS, 4)
+        out[k] = e
+    return out
+
+
 def cpu_baseline(inp, cfg, n_rows: int):
     """The oracle as it stands, on n_rows seeded rows of the workload: loss,
     lse, dH and the rows' dW contribution, i.e. the whole step for those rows."""
@@ -269,7 +289,8 @@ def shard_leg(flce, wl, H, W, cfg, ws, stream, steps: int):
     return {"workload": f"{cfg.name} as vocab shard 1 of 2 (vocab_start={V}, vocab_total={2 * V})",
             "steps": steps, "ms_per_step": round(ms, 3),
             "tflops": round(8.0 * T * d * V / ms / 1e9, 2),
-            "merge_avg_ms": round(merge["total_ms"] / max(1, merge["launches"]), 4)}
+            "merge_avg_ms": round(merge["total_ms"] / max(1, merge["launches"]), 4),
+            "kernels": kernel_table(k, steps, ms)}
 
 
 def fused_leg(flce, wl, plan, H, W, y, ws, stream, steps: int):
@@ -293,6 +314,8 @@ def fused_leg(flce, wl, plan, H, W, y, ws, stream, steps: int):
 
     step()
     torch.cuda.synchronize()
+    flce.flce_timing_collect()
+    flce.flce_timing_enable(True)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -300,10 +323,12 @@ def fused_leg(flce, wl, plan, H, W, y, ws, stream, steps: int):
         step()
     e1.record(stream)
     torch.cuda.synchronize()
+    flce.flce_timing_enable(False)
+    k = flce.flce_timing_collect()
     ms = e0.elapsed_time(e1) / steps
     log(f"  fused call (mean over valid tokens, bf16 dW copy): {ms:.2f} ms/step")
     return {"reduction": "mean_valid", "dW_bf16": True, "steps": steps, "ms_per_step": round(ms, 3),
-            "tflops": round(8.0 * T * d * V / ms / 1e9, 2)}
+            "tflops": round(8.0 * T * d * V / ms / 1e9, 2), "kernels": kernel_table(k, steps, ms)}
 
 
 def scoring_leg(flce, H, W, y, lse, stream, reps: int = 5):
@@ -469,10 +494,10 @@ def main():
         if name in alg_step:
             k["flops"] = alg_step[name] * args.steps
     effective = (2.0 * T * d * V + 6.0 * t_valid * d * V) / (ms / 1e3) / 1e12
-    for name, k in kernels.items():
-        tf = k["flops"] / (k["total_ms"] / 1e3) / 1e12 if k["total_ms"] else 0.0
-        log(f"  {name:10s} launches {k['launches']:5d}  avg {k['total_ms'] / k['launches']:8.3f} ms"
-            f"  share {k['total_ms'] / args.steps / ms:6.1%}  {tf:7.1f} TFLOP/s")
+    for name, e in kernel_table(kernels, args.steps, ms).items():
+        rate = f"{e['tflops']:7.1f} TFLOP/s" if "tflops" in e else f"{e['gbs']:7.1f} GB/s"
+        log(f"  {name:10s} launches {e['launches']:5d}  avg {e['avg_ms']:8.3f} ms"
+            f"  share {e['share']:6.1%}  {rate}")
     dom_name, dom = max(kernels.items(), key=lambda kv: kv[1]["total_ms"])
     avg_ms = dom["total_ms"] / dom["launches"]
     flops_per_launch = dom["flops"] / dom["launches"]
@@ -521,11 +546,7 @@ def main():
                    "vocab_axis_workspace_bytes": int(plan.dz_ws_bytes),
                    "naive_logits_one_copy_bytes": int(plan.naive_logits_bytes),
                    "naive_logits_and_grad_bytes": int(2 * plan.naive_logits_bytes)},
-        "kernels": {k: {"launches": v["launches"], "avg_ms": round(v["total_ms"] / v["launches"], 4),
-                        "share": round(v["total_ms"] / args.steps / ms, 4),
-                        "tflops": round(v["flops"] / (v["total_ms"] / 1e3) / 1e12, 2)
-                        if v["total_ms"] else 0.0}
-                    for k, v in kernels.items()},
+        "kernels": kernel_table(kernels, args.steps, ms),
         "kernel_ms_per_step": round(step_kernel_ms, 3),
         "shard_mode": shard,
         "token_scoring": scoring,

@@ -366,20 +366,38 @@ __global__ void __launch_bounds__(256) shard_merge_kernel(ShardMergeArgs a) {
   a.loss[t] = loss;
 }
 
-// Fixed-order reduction: thread i sums loss[i], loss[i + 1024], ... in double
-// (and, for a mean over the non-ignored tokens, counts them), then a tree over
-// the 1024 threads.  One workgroup; deterministic.  Writes the reduced loss
+// Fixed-order reduction: thread x sums loss[x + 1024 k] in double into eight
+// interleaved partial sums (k mod 8), so that eight independent loads per
+// thread are in flight, then adds them in a fixed tree; for a mean over the
+// non-ignored tokens it also counts them; then a tree over the 1024 threads.
+// One workgroup; deterministic for a given T.  Writes the reduced loss
 // scale * sum (/ count) and the gradient scale of that reduction,
 // scale (/ count); a mean over no tokens is 0 with gradient scale 0.
 __global__ void __launch_bounds__(1024) loss_reduce_kernel(ReduceArgs a) {
   __shared__ double buf[1024];
   __shared__ int64_t cnt[1024];
-  double s = 0.0;
+  constexpr int U = 8;
+  double p[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) p[u] = 0.0;
   int64_t c = 0;
-  for (int64_t i = threadIdx.x; i < a.T; i += 1024) {
-    s += (double)a.loss[i];
+  int64_t i = threadIdx.x;
+  for (; i + (U - 1) * 1024 < a.T; i += U * 1024) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = a.loss[i + u * 1024];
+    if (a.mean_valid) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) c += a.y[i + u * 1024] != a.ignore_index ? 1 : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) p[u] += (double)v[u];
+  }
+  for (int u = 0; i < a.T; i += 1024, ++u) {  // fewer than U left for this thread
+    p[u] += (double)a.loss[i];
     if (a.mean_valid) c += a.y[i] != a.ignore_index ? 1 : 0;
   }
+  const double s = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
   buf[threadIdx.x] = s;
   cnt[threadIdx.x] = c;
   __syncthreads();

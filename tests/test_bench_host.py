@@ -119,3 +119,13 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one MI355X" in r.stderr
+
+
+def test_kernel_table_rates(bench):
+    kernels = {"bwd_dw": dict(launches=4, total_ms=8.0, flops=4 * 2e12, bytes=4e9),
+               "fwd_merge": dict(launches=2, total_ms=0.01, flops=0.0, bytes=2 * 3.2e7)}
+    t = bench.kernel_table(kernels, steps=2, step_ms=10.0)
+    # 8 TFLOP in 8 ms -> 1,000 TFLOP/s; 64 MB in 10 us -> 6,400 GB/s = 0.8 of 8 TB/s
+    assert t["bwd_dw"]["tflops"] == 1000.0 and "gbs" not in t["bwd_dw"]
+    assert t["bwd_dw"]["avg_ms"] == 2.0 and t["bwd_dw"]["share"] == 0.4
+    assert t["fwd_merge"]["gbs"] == 6400.0 and t["fwd_merge"]["hbm_frac"] == 0.8
