@@ -24,6 +24,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import struct
 import sys
 import time
 
@@ -114,7 +115,6 @@ def measured_traffic(kernel: str, workload: str, plan_key: dict):
 
 def elf_section(path: str, name: str):
     """Bytes of the named section of a 64-bit little-endian ELF file, or None."""
-    import struct
     data = open(path, "rb").read()
     if data[:4] != b"\x7fELF" or data[4] != 2 or data[5] != 1:
         return None
@@ -143,7 +143,7 @@ def device_code_digest(lib_path: str = None):
         lib_path = _lib.LIB_PATH
     try:
         code = elf_section(lib_path, ".hip_fatbin")
-    except OSError:
+    except (OSError, ValueError, IndexError, struct.error):
         return None
     return None if code is None else hashlib.sha256(code).hexdigest()
 

@@ -129,3 +129,11 @@ def test_kernel_table_rates(bench):
     assert t["bwd_dw"]["tflops"] == 1000.0 and "gbs" not in t["bwd_dw"]
     assert t["bwd_dw"]["avg_ms"] == 2.0 and t["bwd_dw"]["share"] == 0.4
     assert t["fwd_merge"]["gbs"] == 6400.0 and t["fwd_merge"]["hbm_frac"] == 0.8
+
+
+def test_device_code_digest_of_a_broken_file_is_none(bench, tmp_path):
+    (tmp_path / "trunc.so").write_bytes(b"\x7fELF\x02\x01" + b"\0" * 20)
+    (tmp_path / "text.so").write_bytes(b"not a library")
+    assert bench.device_code_digest(str(tmp_path / "trunc.so")) is None
+    assert bench.device_code_digest(str(tmp_path / "text.so")) is None
+    assert bench.device_code_digest(str(tmp_path / "missing.so")) is None
