@@ -75,7 +75,11 @@ def cpu_baseline(inp, cfg, n_rows: int):
                        if i.get("user_api") == "blas"] or [1])
     except Exception:  # threadpoolctl missing: report the core count
         threads = os.cpu_count() or 1
-    rows = wl.sample_rows(cfg, n_rows)
+    if cfg in wl.CONFIGS:
+        rows = wl.sample_rows(cfg, n_rows)
+    else:
+        rows = np.sort(np.random.default_rng(cfg.seed_base).choice(cfg.T, min(n_rows, cfg.T),
+                                                                   replace=False))
     Hs = inp.H_f32()[rows]
     Wf = inp.W_f32()
     ys = inp.y[rows]
@@ -383,6 +387,11 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3, help="workload index (default 3)")
+    ap.add_argument("--shape", type=int, nargs=3, metavar=("T", "d", "V"),
+                    help="a synthetic workload of this shape instead of --config: H ~ N(0,1), "
+                         "W ~ N(0,0.02^2), uniform targets, none ignored, grad scale 1")
+    ap.add_argument("--dtype", choices=("bf16", "f32"), default="bf16",
+                    help="element type of the --shape workload")
     ap.add_argument("--shard-steps", type=int, default=3,
                     help="steps of each extra leg (vocab shard: W as rank 1 of 2 of a 2V-id "
                          "vocabulary; fused call; token scoring); 0 skips them")
@@ -426,10 +435,16 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(3)
     flce.load()
-    cfg = wl.CONFIGS[args.config]
+    if args.shape:
+        T_, d_, V_ = args.shape
+        cfg = wl.Config(f"synthetic_{args.dtype}_T{T_}_d{d_}_V{V_}", T_, d_, V_, args.dtype, 0.02,
+                        "uniform")
+    else:
+        cfg = wl.CONFIGS[args.config]
     log(f"workload {cfg.name}: generating inputs")
     t0 = time.perf_counter()
-    inp = wl.config_inputs(cfg)
+    inp = (wl.config_inputs(cfg) if cfg in wl.CONFIGS else
+           wl.make_inputs(cfg.T, cfg.d, cfg.V, cfg.dtype, cfg.seed_base, sigma_w=cfg.sigma_w))
     log(f"  inputs ready in {time.perf_counter() - t0:.1f} s")
     dev = torch.device("cuda:0")
     bf16 = cfg.dtype == wl.DTYPE_BF16
