@@ -504,7 +504,7 @@ def main():
     # contraction kernels per step are 2*T_valid*d*V each (2*T*d*V forward).
     t_valid = int((inp.y != wl.IGNORE_INDEX).sum())
     alg_step = {"fwd_sweep": 2.0 * T * d * V, "bwd_dz": 2.0 * t_valid * d * V,
-                "bwd_dh": 2.0 * t_valid * d * V, "bwd_dw": 2.0 * t_valid * d * V}
+                "bwd_dhdw": 4.0 * t_valid * d * V}
     for name, k in kernels.items():
         if name in alg_step:
             k["flops"] = alg_step[name] * args.steps

@@ -66,13 +66,12 @@ flce_status_t hip_fail(hipError_t e, const char* what) {
 
 // ------------------------------------------------------------ kernel timing
 enum KernelId {
-  K_FWD_SWEEP, K_FWD_MERGE, K_LOSS_SUM, K_BWD_DZ, K_BWD_DH, K_BWD_DW, K_FILL, K_SHARD_MERGE,
-  K_TOKEN_LOGIT, K_CAST, K_TRANSPOSE, K_COMPACT, K_DH_REDUCE, K_COUNT
+  K_FWD_SWEEP, K_FWD_MERGE, K_LOSS_SUM, K_BWD_DZ, K_BWD_DHDW, K_DH_REDUCE, K_FILL,
+  K_SHARD_MERGE, K_TOKEN_LOGIT, K_CAST, K_TRANSPOSE, K_COMPACT, K_COUNT
 };
-const char* const kKernelNames[K_COUNT] = {"fwd_sweep", "fwd_merge", "loss_sum",    "bwd_dz",
-                                           "bwd_dh",    "bwd_dw",    "fill_zero",   "shard_merge",
-                                           "token_logit", "cast_bf16",   "gather_h",
-                                           "compact", "dh_reduce"};
+const char* const kKernelNames[K_COUNT] = {
+    "fwd_sweep", "fwd_merge",   "loss_sum",  "bwd_dz",   "bwd_dhdw", "dh_reduce",
+    "fill_zero", "shard_merge", "token_logit", "cast_bf16", "gather_h", "compact"};
 
 struct TimingRec {
   int kid;
@@ -392,22 +391,6 @@ flce_status_t backward_impl(const flce_plan_t* plan, const void* H, const void* 
       h.dh_acc = dh_acc;
       h.dH = dH;
       h.part = dh_part;
-      Timed t_dh(s, K_BWD_DH, 2.0 * tc * dd * vc,
-                 tc * vc * esz + vc * dd * esz +
-                     tc * dd * (h.mode == 1 || h.mode == 2 ? 4.0 : 0.0) +
-                     tc * dd * (h.mode >= 2 ? esz : 4.0));
-      e = flce::launch_bwd_dh(h, bf16, s);
-      t_dh.done();
-      if (e != hipSuccess) return hip_fail(e, "dH launch");
-      if (dh_part) {
-        // sums the parts when the device split the K loop (reads them all
-        // once, then the mode's accumulator and dH traffic)
-        Timed t_red(s, K_DH_REDUCE, 0, tc * dd * 4.0 * 2);
-        e = flce::launch_bwd_dh_reduce(h, bf16, s);
-        t_red.done();
-        if (e != hipSuccess) return hip_fail(e, "dH reduce launch");
-      }
-
       flce::DwArgs w;
       w.dz = dz;
       w.Ht = ht;
@@ -421,11 +404,23 @@ flce_status_t backward_impl(const flce_plan_t* plan, const void* H, const void* 
       w.n_ntiles = (int)cdiv(v_count, ti.dw_bn);
       w.accumulate = (b > 0 || accumulate_dW) ? 1 : 0;
       w.dW = dW;
-      Timed t_dw(s, K_BWD_DW, 2.0 * tc * dd * vc,
-                 tc * vc * esz + tc * dd * esz + vc * dd * (w.accumulate ? 8.0 : 4.0));
-      e = flce::launch_bwd_dw(w, bf16, s);
-      t_dw.done();
-      if (e != hipSuccess) return hip_fail(e, "dW launch");
+      // dH and dW in one launch (both only read this slab's dZ)
+      Timed t_hw(s, K_BWD_DHDW, 4.0 * tc * dd * vc,
+                 2.0 * tc * vc * esz + vc * dd * esz +
+                     tc * dd * (h.mode == 1 || h.mode == 2 ? 4.0 : 0.0) +
+                     tc * dd * (h.mode >= 2 ? esz : 4.0) + tc * dd * esz +
+                     vc * dd * (w.accumulate ? 8.0 : 4.0));
+      e = flce::launch_bwd_dhdw(h, w, bf16, s);
+      t_hw.done();
+      if (e != hipSuccess) return hip_fail(e, "dH/dW launch");
+      if (dh_part) {
+        // sums the parts when the device split dH's K loop (reads them all
+        // once, then the mode's accumulator and dH traffic)
+        Timed t_red(s, K_DH_REDUCE, 0, tc * dd * 4.0 * 2);
+        e = flce::launch_bwd_dh_reduce(h, bf16, s);
+        t_red.done();
+        if (e != hipSuccess) return hip_fail(e, "dH reduce launch");
+      }
     }
   }
   return ok();

@@ -21,11 +21,14 @@
 //   gather_block one token block of H in that order, as rows and transposed.
 //   bwd_dz       recomputed logits tile -> dZ = g * (exp(z - lse) - onehot),
 //                stored (bf16 or fp32) to the [block x slab] workspace.
-//   bwd_dh       dH_block (+)= dZ W_slab   (fp32 accumulate, cast at the end);
-//                cuts the slab's K loop into parts when the block has too few
-//                tiles to occupy the GPU.
-//   bwd_dh_reduce  sums those parts in order and applies the accumulator mode.
-//   bwd_dw       dW_slab^T (+)= H_block^T dZ (fp32, deterministic block order).
+//   bwd_dhdw     one launch of both contractions of a block and slab (dH
+//                workgroups first, so a partial last round of dH's long tiles
+//                fills with dW's short ones):
+//                dH_block (+)= dZ W_slab   (fp32 accumulate, cast at the end;
+//                the slab's K loop cut into parts when the block has too few
+//                tiles to occupy the GPU), and
+//                dW_slab^T (+)= H_block^T dZ (fp32, deterministic block order).
+//   bwd_dh_reduce  sums dH's parts in order and applies the accumulator mode.
 //   token_logit  gathered h . w minus lse for given tokens (scoring), up to
 //                eight gathered rows per pass.
 //   cast_bf16    optional bf16 copy of dW.
@@ -660,10 +663,10 @@ __device__ __forceinline__ void dh_store(const DhArgs& a, const TL& tile, int64_
   }
 }
 
+// One dH workgroup; `bid` is its index among the dH workgroups of the launch.
 template <typename E>
-__global__ void __launch_bounds__(DhCfg<E>::T::NT, 1) bwd_dh_kernel(DhArgs a) {
+__device__ __forceinline__ void dh_body(const DhArgs& a, int bid, char* lds) {
   using TL = typename DhCfg<E>::T;
-  extern __shared__ __attribute__((aligned(16))) char lds[];
   constexpr int ESZ = TL::ESZ;
   const int t_count = block_count(a.blk);
   const int act_m = (t_count + TL::BM - 1) / TL::BM;
@@ -671,7 +674,7 @@ __global__ void __launch_bounds__(DhCfg<E>::T::NT, 1) bwd_dh_kernel(DhArgs a) {
   // split-major virtual token tiles: the workgroups an XCD runs together
   // share one part's W panels
   int tv, tn;
-  if (!xcd_tile(blockIdx.x, act_m * S, a.n_ntiles, 4, tv, tn)) return;
+  if (!xcd_tile(bid, act_m * S, a.n_ntiles, 4, tv, tn)) return;
   const int sp = tv / act_m, tm = tv % act_m;
   const int64_t tl0 = (int64_t)tm * TL::BM;  // token within block
   const int64_t n0 = (int64_t)tn * TL::BN;   // hidden index
@@ -767,13 +770,13 @@ __global__ void __launch_bounds__(256) bwd_dh_reduce_kernel(DhArgs a) {
 // one dW row (16-byte loads and stores).  accumulate: 0 = overwrite, 1 = add
 // to dW (the MFMA accumulators start from the stored dW tile, so the
 // epilogue only stores).
+// One dW workgroup; `bid` is its index among the dW workgroups of the launch.
 template <typename E>
-__global__ void __launch_bounds__(DwCfg<E>::T::NT, 1) bwd_dw_kernel(DwArgs a) {
+__device__ __forceinline__ void dw_body(const DwArgs& a, int bid, char* lds) {
   using TL = typename DwCfg<E>::T;
-  extern __shared__ __attribute__((aligned(16))) char lds[];
   constexpr int ESZ = TL::ESZ;
   int tm, tn;
-  if (!xcd_tile(blockIdx.x, a.n_mtiles, a.n_ntiles, 8, tm, tn)) return;
+  if (!xcd_tile(bid, a.n_mtiles, a.n_ntiles, 8, tm, tn)) return;
   const int wave = threadIdx.x >> 6;
   const int wm = wave / TL::WN, wn = wave % TL::WN;
   const int64_t n0 = (int64_t)tm * TL::BM;   // hidden
@@ -828,6 +831,20 @@ __global__ void __launch_bounds__(DwCfg<E>::T::NT, 1) bwd_dw_kernel(DwArgs a) {
                       tile.acc[i][j][4 * q + 3]};
       }
   }
+}
+
+// dH and dW of one block and slab in a single launch: both only read the
+// slab's dZ and write different outputs.  The dH workgroups come first, so the
+// compute units that a partial last round of the long dH tiles leaves idle
+// take the short dW tiles instead of waiting for the next launch.
+template <typename E>
+__global__ void __launch_bounds__(DhCfg<E>::T::NT, 1) bwd_dhdw_kernel(DhArgs h, DwArgs w,
+                                                                     int dh_grid) {
+  static_assert(DhCfg<E>::T::NT == DwCfg<E>::T::NT &&
+                DhCfg<E>::T::LDS_BYTES == DwCfg<E>::T::LDS_BYTES, "one launch shape");
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  if ((int)blockIdx.x < dh_grid) dh_body<E>(h, blockIdx.x, lds);
+  else dw_body<E>(w, blockIdx.x - dh_grid, lds);
 }
 
 __global__ void __launch_bounds__(256) fill_zero_kernel(float* p, int64_t n) {
@@ -1165,19 +1182,26 @@ hipError_t launch_bwd_dz(const DzArgs& a, bool bf16, hipStream_t s) {
 }
 
 template <typename E>
-static hipError_t launch_dh(const DhArgs& a, hipStream_t s) {
-  using TL = typename DhCfg<E>::T;
-  // unsplit: every tile of the full block; split: at most kDhSplitSlots
-  // (part, tile) pairs, whatever the device's token count
+static int dh_grid(const DhArgs& a) {
   int tiles = a.n_mtiles * a.n_ntiles;
   if (a.part && tiles < kDhSplitSlots) tiles = kDhSplitSlots;
-  hipError_t e = set_lds(bwd_dh_kernel<E>, TL::LDS_BYTES);
-  if (e != hipSuccess) return e;
-  return launch(bwd_dh_kernel<E>, xcd_grid(tiles, 1), TL::NT, TL::LDS_BYTES, s, a);
+  return xcd_grid(tiles, 1);
 }
 
-hipError_t launch_bwd_dh(const DhArgs& a, bool bf16, hipStream_t s) {
-  return bf16 ? launch_dh<__bf16>(a, s) : launch_dh<float>(a, s);
+template <typename E>
+static hipError_t launch_dhdw(const DhArgs& h, const DwArgs& w, hipStream_t s) {
+  using TL = typename DhCfg<E>::T;
+  hipError_t e = set_lds(bwd_dhdw_kernel<E>, TL::LDS_BYTES);
+  if (e != hipSuccess) return e;
+  const int gh = dh_grid<E>(h);
+  const int gw = xcd_grid(w.n_mtiles, w.n_ntiles);
+  if (gh + gw <= 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_dhdw_kernel<E>, dim3(gh + gw), dim3(TL::NT), TL::LDS_BYTES, s, h, w, gh);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dhdw(const DhArgs& h, const DwArgs& w, bool bf16, hipStream_t s) {
+  return bf16 ? launch_dhdw<__bf16>(h, w, s) : launch_dhdw<float>(h, w, s);
 }
 
 template <typename E>
@@ -1196,20 +1220,6 @@ hipError_t launch_bwd_dh_reduce(const DhArgs& a, bool bf16, hipStream_t s) {
 }
 
 int dh_split_slots() { return kDhSplitSlots; }
-
-hipError_t launch_bwd_dw(const DwArgs& a, bool bf16, hipStream_t s) {
-  const int grid = xcd_grid(a.n_mtiles, a.n_ntiles);
-  if (bf16) {
-    using TL = DwCfg<__bf16>::T;
-    hipError_t e = set_lds(bwd_dw_kernel<__bf16>, TL::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    return launch(bwd_dw_kernel<__bf16>, grid, TL::NT, TL::LDS_BYTES, s, a);
-  }
-  using TL = DwCfg<float>::T;
-  hipError_t e = set_lds(bwd_dw_kernel<float>, TL::LDS_BYTES);
-  if (e != hipSuccess) return e;
-  return launch(bwd_dw_kernel<float>, grid, TL::NT, TL::LDS_BYTES, s, a);
-}
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;

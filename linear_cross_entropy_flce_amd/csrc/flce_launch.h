@@ -136,12 +136,13 @@ struct ReduceArgs {
 hipError_t launch_loss_reduce(const ReduceArgs& a, hipStream_t s);
 hipError_t launch_cast_bf16(const float* src, void* dst, int64_t n, hipStream_t s);
 hipError_t launch_bwd_dz(const DzArgs& a, bool bf16, hipStream_t s);
-hipError_t launch_bwd_dh(const DhArgs& a, bool bf16, hipStream_t s);
 // Sums a split dH's parts and applies the mode (nothing when unsplit); launch
-// after launch_bwd_dh with the same arguments.
+// after launch_bwd_dhdw with the same dH arguments.
 hipError_t launch_bwd_dh_reduce(const DhArgs& a, bool bf16, hipStream_t s);
 int dh_split_slots();
-hipError_t launch_bwd_dw(const DwArgs& a, bool bf16, hipStream_t s);
+// dH and dW of one block and slab as a single launch (dH workgroups first);
+// launch_bwd_dh_reduce follows when dH splits.
+hipError_t launch_bwd_dhdw(const DhArgs& h, const DwArgs& w, bool bf16, hipStream_t s);
 // Scoring of given tokens: out[t * K + k] = H[t] . W[tokens[t * K + k]] - lse[t]
 // (lse NULL: the logit itself).
 struct TokenArgs {

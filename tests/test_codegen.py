@@ -34,7 +34,7 @@ def _kernels(text):
 
 def test_every_kernel_is_there(asm):
     names = " ".join(_kernels(asm))
-    for k in ("fwd_sweep", "fwd_merge", "bwd_dz", "bwd_dh", "bwd_dh_reduce", "bwd_dw",
+    for k in ("fwd_sweep", "fwd_merge", "bwd_dz", "bwd_dhdw", "bwd_dh_reduce",
               "token_logit", "loss_reduce", "cast_bf16", "compact_count", "gather_block"):
         assert k in names, k
 
