@@ -435,6 +435,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(3)
     flce.load()
+    torch.cuda.init()
+    free_before = torch.cuda.mem_get_info()[0]  # hipMemGetInfo before any of the step's buffers
     if args.shape:
         T_, d_, V_ = args.shape
         cfg = wl.Config(f"synthetic_{args.dtype}_T{T_}_d{d_}_V{V_}", T_, d_, V_, args.dtype, 0.02,
@@ -493,6 +495,7 @@ def main():
     kernels = flce.flce_timing_collect()
     ms = ev0.elapsed_time(ev1) / args.steps
     peak_mem = torch.cuda.max_memory_allocated()
+    device_used = free_before - torch.cuda.mem_get_info()[0]
     counted = 8.0 * T * d * V
     value = counted / (ms / 1e3) / 1e12
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
@@ -557,6 +560,9 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "memory": {"peak_allocated_bytes": int(peak_mem),
+                   # hipMemGetInfo delta: what the step's process holds on the device
+                   # (inputs, outputs, workspace, torch's cached blocks and context)
+                   "device_used_delta_bytes": int(device_used),
                    "workspace_bytes": int(plan.ws_bytes),
                    "vocab_axis_workspace_bytes": int(plan.dz_ws_bytes),
                    "naive_logits_one_copy_bytes": int(plan.naive_logits_bytes),
