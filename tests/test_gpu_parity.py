@@ -308,7 +308,7 @@ def test_config_full(ci):
 @pytest.mark.timeout(900)
 def test_config2_full():
     cfg = wl.CONFIGS[2]
-    log(f"config 2 {cfg.name}: inputs")
+    log(f"{cfg.name}: inputs")
     inp = wl.config_inputs(cfg)
     ls, gs = cfg.scales()
     got = run_gpu(inp, loss_scale=ls, grad_scale=gs)
