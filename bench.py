@@ -93,7 +93,9 @@ def cpu_baseline(inp, cfg, n_rows: int):
             "sample": f"{n_rows} seeded token rows of the same workload (all {cfg.V} vocab "
                       f"columns, d={cfg.d}): numpy float64 logits, lse, loss, dH and the rows' dW; "
                       f"{dt:.2f} s; counted as 8*rows*d*V like the GPU figure",
-            "seconds": dt, "host_cpus": os.cpu_count()}
+            "seconds": dt, "host_cpus": os.cpu_count(),
+            # extrapolation, not a measurement: the sample's rate over the whole step
+            "extrapolated_full_step_s": round(8.0 * cfg.T * cfg.d * cfg.V / (counted / dt), 1)}
 
 
 def measured_traffic(kernel: str, workload: str, plan_key: dict):
