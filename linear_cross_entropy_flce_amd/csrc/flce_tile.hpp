@@ -14,7 +14,8 @@
 // Global -> LDS, three loaders (one barrier per stage each):
 //   - register-staged double buffer (DMA = false, NS = 2; what every kernel
 //     uses): buffer_load_dwordx4 into VGPRs 1.5 stages ahead, ds_write into
-//     the other LDS stage;
+//     the other LDS stage, with an explicit MFMA / LDS / global-load
+//     interleave in the branch-free steady state;
 //   - two-stage direct DMA (buffer_load_dwordx4 ... lds, no VGPR staging);
 //   - a DMA ring of NS > 2 stages running NS - 1 stages ahead.
 // LDS layouts, the same for all three:
@@ -504,7 +505,26 @@ struct Tile {
   //     buffer after the second step and the loads of the stage after it are
   //     issued right then (global latency hides behind ~1.5 stages);
   //   - one barrier per stage.
-  template <int P>
+  // Stages whose loads two ahead lie wholly below K run a branch-free body
+  // (STEADY): one scheduling region per fragment step, in which the MFMAs
+  // alternate with that step's LDS reads and, in the second step, with the
+  // next stage's LDS writes and global loads; the last step issues half its
+  // MFMAs, meets the barrier, reads the next stage's first fragments and
+  // then issues its other half, so the matrix unit has work while those
+  // reads are in flight.  The last few stages run the general body, whose
+  // bounds checks and conditions are branches.
+  __device__ __forceinline__ void mma_rows(const u32x4_t* fa, const u32x4_t* fb, int i0, int i1) {
+#pragma unroll
+    for (int i = i0; i < i1; ++i)
+#pragma unroll
+      for (int j = 0; j < NI; ++j) mma(acc[i][j], fa[i], fb[j]);
+  }
+
+  // sched_group_barrier masks (LLVM AMDGPU): instruction classes
+  static constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100,
+                       kSchedDsWrite = 0x200;
+
+  template <int P, bool STEADY>
   __device__ __forceinline__ void regs_stage(const Operand& A, const Operand& B, char* lds, int kt,
                                              int nk, int K, int wm, int wn, const uint32_t* va,
                                              const int* ka, const uint32_t* vb, const int* kb,
@@ -514,27 +534,67 @@ struct Tile {
     const char* cb = lds + 2 * A_BYTES + P * B_BYTES;
     char* na = lds + (1 - P) * A_BYTES;
     char* nb = lds + 2 * A_BYTES + (1 - P) * B_BYTES;
+    if constexpr (STEADY && ESZ == 2) {
+      constexpr int NR = (A_KC ? MI : 2 * MI) + (B_KC ? NI : 2 * NI);  // LDS reads per step
+      constexpr int NM = MI * NI;                                     // MFMAs per step
+      constexpr int NL = A_LD + B_LD;                                 // loads per stage
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) {
+          read_frags(ca, cb, wm, wn, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+          mma_all(fa[ks & 1], fb[ks & 1]);
+          if (ks == 1) {
+            lstore<A_KC, BM, A_PITCH, A_LD>(na, ra);
+            lstore<B_KC, BN, B_PITCH, B_LD>(nb, rb);
+            const int k0 = (kt + 2) * BK;
+            gload_fast<A_KC, A_LD>(A, va, ka, k0, true, ra);
+            gload_fast<B_KC, B_LD>(B, vb, kb, k0, true, rb);
+          }
+#pragma unroll
+          for (int q = 0; q < NM; ++q) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            if (q < NR) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            if (ks == 1 && q < NL) {
+              __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        } else {
+          mma_rows(fa[ks & 1], fb[ks & 1], 0, MI / 2);
+          __builtin_amdgcn_sched_barrier(0);
+          __syncthreads();
+          read_frags(na, nb, wm, wn, 0, fa[0], fb[0]);
+          mma_rows(fa[ks & 1], fb[ks & 1], MI / 2, MI);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, NR, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, NM / 2, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (ks + 1 < KS) read_frags(ca, cb, wm, wn, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
       mma_all(fa[ks & 1], fb[ks & 1]);
-      if (ks == 1 && kt + 1 < nk) {
+      if (ks == 1 && (STEADY || kt + 1 < nk)) {
         lstore<A_KC, BM, A_PITCH, A_LD>(na, ra);
         lstore<B_KC, BN, B_PITCH, B_LD>(nb, rb);
-        if (kt + 2 < nk) {
+        if (STEADY || kt + 2 < nk) {
           const int k0 = (kt + 2) * BK;
-          const bool full = k0 + BK <= K;
+          const bool full = STEADY || k0 + BK <= K;
           gload_fast<A_KC, A_LD>(A, va, ka, k0, full, ra);
           gload_fast<B_KC, B_LD>(B, vb, kb, k0, full, rb);
         }
       }
     }
     __syncthreads();
-    if (kt + 1 < nk) read_frags(na, nb, wm, wn, 0, fa[0], fb[0]);
+    if (STEADY || kt + 1 < nk) read_frags(na, nb, wm, wn, 0, fa[0], fb[0]);
   }
 
   __device__ __forceinline__ void mainloop_regs(const Operand& A, const Operand& B, int K, char* lds) {
     static_assert(KS % 2 == 0 && KS >= 2, "fragment double buffer needs an even step count");
+    static_assert(MI % 2 == 0, "the last step's MFMAs are issued in two halves");
     const int wave = threadIdx.x >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int nk = (K + BK - 1) / BK;
@@ -555,9 +615,17 @@ struct Tile {
     __syncthreads();
     u32x4_t fa[2][MI], fb[2][NI];
     read_frags(lds, lds + 2 * A_BYTES, wm, wn, 0, fa[0], fb[0]);
-    for (int kt = 0; kt < nk; kt += 2) {
-      regs_stage<0>(A, B, lds, kt, nk, K, wm, wn, va, ka, vb, kb, ra, rb, fa, fb);
-      if (kt + 1 < nk) regs_stage<1>(A, B, lds, kt + 1, nk, K, wm, wn, va, ka, vb, kb, ra, rb, fa, fb);
+    // a pair of stages (kt, kt + 1) is steady when the stages they load,
+    // kt + 2 and kt + 3, are whole: (kt + 4) * BK <= K
+    const int nfull = K / BK;
+    int kt = 0;
+    for (; kt + 4 <= nfull; kt += 2) {
+      regs_stage<0, true>(A, B, lds, kt, nk, K, wm, wn, va, ka, vb, kb, ra, rb, fa, fb);
+      regs_stage<1, true>(A, B, lds, kt + 1, nk, K, wm, wn, va, ka, vb, kb, ra, rb, fa, fb);
+    }
+    for (; kt < nk; kt += 2) {
+      regs_stage<0, false>(A, B, lds, kt, nk, K, wm, wn, va, ka, vb, kb, ra, rb, fa, fb);
+      if (kt + 1 < nk) regs_stage<1, false>(A, B, lds, kt + 1, nk, K, wm, wn, va, ka, vb, kb, ra, rb, fa, fb);
     }
   }
 
