@@ -507,8 +507,9 @@ struct Tile {
   //   - one barrier per stage.
   // Stages whose loads two ahead lie wholly below K run a branch-free body
   // (STEADY): one scheduling region per fragment step, in which the MFMAs
-  // alternate with that step's LDS reads and, in the second step, with the
-  // next stage's LDS writes and global loads; the last step issues half its
+  // alternate with that step's LDS reads and, in the first step, with the
+  // next stage's LDS writes and global loads (issued there, the loads run
+  // ~1.75 stages ahead of their use); the last step issues half its
   // MFMAs, meets the barrier, reads the next stage's first fragments and
   // then issues its other half, so the matrix unit has work while those
   // reads are in flight.  The last few stages run the general body, whose
@@ -543,7 +544,7 @@ struct Tile {
         if (ks + 1 < KS) {
           read_frags(ca, cb, wm, wn, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
           mma_all(fa[ks & 1], fb[ks & 1]);
-          if (ks == 1) {
+          if (ks == 0) {
             lstore<A_KC, BM, A_PITCH, A_LD>(na, ra);
             lstore<B_KC, BN, B_PITCH, B_LD>(nb, rb);
             const int k0 = (kt + 2) * BK;
@@ -554,7 +555,7 @@ struct Tile {
           for (int q = 0; q < NM; ++q) {
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
             if (q < NR) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-            if (ks == 1 && q < NL) {
+            if (ks == 0 && q < NL) {
               __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
               __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
             }
