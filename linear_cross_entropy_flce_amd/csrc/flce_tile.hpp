@@ -535,9 +535,12 @@ struct Tile {
     const char* cb = lds + 2 * A_BYTES + P * B_BYTES;
     char* na = lds + (1 - P) * A_BYTES;
     char* nb = lds + 2 * A_BYTES + (1 - P) * B_BYTES;
-    if constexpr (STEADY && ESZ == 2) {
-      constexpr int NR = (A_KC ? MI : 2 * MI) + (B_KC ? NI : 2 * NI);  // LDS reads per step
-      constexpr int NM = MI * NI;                                     // MFMAs per step
+    if constexpr (STEADY) {
+      // LDS reads per step: one per K-contiguous fragment; two transpose
+      // reads (bf16) or four scalar reads (fp32) per MN-contiguous one
+      constexpr int RMC = ESZ == 2 ? 2 : 4;
+      constexpr int NR = (A_KC ? MI : RMC * MI) + (B_KC ? NI : RMC * NI);
+      constexpr int NM = MI * NI * (ESZ == 2 ? 1 : 4);                // MFMAs per step
       constexpr int NL = A_LD + B_LD;                                 // loads per stage
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
