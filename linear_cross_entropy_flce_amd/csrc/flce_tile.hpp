@@ -581,19 +581,19 @@ struct Tile {
     for (int ks = 0; ks < KS; ++ks) {
       if (ks + 1 < KS) read_frags(ca, cb, wm, wn, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
       mma_all(fa[ks & 1], fb[ks & 1]);
-      if (ks == 1 && (STEADY || kt + 1 < nk)) {
+      if (ks == 1 && kt + 1 < nk) {
         lstore<A_KC, BM, A_PITCH, A_LD>(na, ra);
         lstore<B_KC, BN, B_PITCH, B_LD>(nb, rb);
-        if (STEADY || kt + 2 < nk) {
+        if (kt + 2 < nk) {
           const int k0 = (kt + 2) * BK;
-          const bool full = STEADY || k0 + BK <= K;
+          const bool full = k0 + BK <= K;
           gload_fast<A_KC, A_LD>(A, va, ka, k0, full, ra);
           gload_fast<B_KC, B_LD>(B, vb, kb, k0, full, rb);
         }
       }
     }
     __syncthreads();
-    if (STEADY || kt + 1 < nk) read_frags(na, nb, wm, wn, 0, fa[0], fb[0]);
+    if (kt + 1 < nk) read_frags(na, nb, wm, wn, 0, fa[0], fb[0]);
   }
 
   __device__ __forceinline__ void mainloop_regs(const Operand& A, const Operand& B, int K, char* lds) {
