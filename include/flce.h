@@ -24,7 +24,9 @@
  *   - Targets y are int64 [T].  y_i == ignore_index marks an ignored token:
  *     loss_i = 0 and its dZ row is zero (its lse is still computed).  A
  *     target outside [0, V) that is not ignore_index is a precondition
- *     violation: that token's loss, and the gradients it touches, are NaN.
+ *     violation: that token's loss and its dH row are NaN, and so is every
+ *     element of dW (its dZ row is NaN, and each dW row sums over all tokens);
+ *     its lse, and the loss and dH rows of the other tokens, are unaffected.
  *   - Every pointer argument except the host plan is device memory owned by
  *     the caller.  The library never allocates device memory, never
  *     synchronises the host, and keeps no state between calls other than a
@@ -95,6 +97,11 @@ typedef struct flce_plan {
 } flce_plan_t;
 
 /* flce_plan -- choose tiles, splits, token block and vocab slab.
+ * Section 3 of the first page bounds the method's vocab-axis residency by one
+ * token block times the vocabulary ([block x vocab], under a gigabyte, down
+ * from [tokens x vocab]); section 8 asks for tiles sized to 64-lane waves and
+ * LDS.  The plan fixes the [bwd_block x bwd_slab] buffer that bounds this
+ * residency, and the MFMA tile shapes the kernels use.
  *   T, d, V : problem size (see requirements above).
  *   dtype   : element type of H, W, dH.
  *   vocab_ws_cap_bytes : upper bound for the backward workspace (the dZ
@@ -124,6 +131,10 @@ flce_status_t flce_forward(const flce_plan_t* plan, const void* H, const void* W
                            void* stream);
 
 /* flce_backward -- dH and dW of grad_scale * sum_i loss_i.
+ * Section 3 of the first page: the backward recomputes each logit tile from
+ * the still-resident H and W, forms dZ = softmax(Z) - onehot(y) for that tile
+ * and contracts it into dH = dZ W and dW^T = H^T dZ; here dZ lives for one
+ * [bwd_block x bwd_slab] tile buffer at a time (bf16 for bf16 inputs).
  *   Ignored tokens contribute nothing (their dZ rows are zero), so the
  *   backward compacts the other tokens on the device (ascending order) and
  *   runs its contractions over them only; their dH rows are written as 0.

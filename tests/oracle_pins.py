@@ -232,6 +232,46 @@ def pin_rejects_bad_target(orc):
     raise AssertionError("out-of-range target was accepted")
 
 
+def pin_backward(orc):
+    """backward() returns (dH, dW) of g * sum_i loss_i, in that order: checked
+    against central differences of the loss (T != V != d, so a swapped pair
+    fails on shape alone), against the W = 0 closed form of dW, and for its
+    linearity in g (dZ = g (softmax - onehot), first page section 3)."""
+    T, d, V, g, eps = 4, 3, 6, 0.6, 1e-6
+    H, W, y = _tiny(11, T, d, V, sigma_w=0.9, n_ignored=1)
+    dH, dW = orc.backward(H, W, y, IGN, g)
+    assert dH.shape == (T, d) and dW.shape == (V, d)
+
+    def L(Hx, Wx):
+        loss, _ = orc.forward(Hx, Wx, y, IGN)
+        return g * math.fsum(loss)
+
+    for i in range(T):
+        for k in range(d):
+            Hp, Hm = H.copy(), H.copy()
+            Hp[i, k] += eps
+            Hm[i, k] -= eps
+            assert abs(dH[i, k] - (L(Hp, W) - L(Hm, W)) / (2 * eps)) < 1e-7
+    for j in range(V):
+        for k in range(d):
+            Wp, Wm = W.copy(), W.copy()
+            Wp[j, k] += eps
+            Wm[j, k] -= eps
+            assert abs(dW[j, k] - (L(H, Wp) - L(H, Wm)) / (2 * eps)) < 1e-7
+    # linear in g: twice the scale, twice the gradients
+    dH2, dW2 = orc.backward(H, W, y, IGN, 2 * g)
+    assert np.allclose(dH2, 2 * dH, atol=1e-14, rtol=1e-12)
+    assert np.allclose(dW2, 2 * dW, atol=1e-14, rtol=1e-12)
+    # W = 0: dH = 0 and dW_j = g * sum over valid i of (1/V - [y_i = j]) h_i
+    dH0, dW0 = orc.backward(H, np.zeros((V, d)), y, IGN, g)
+    assert np.all(dH0 == 0.0)
+    for j in range(V):
+        e = sum(g * ((1.0 / V) - (1.0 if y[i] == j else 0.0)) * H[i]
+                for i in range(T) if y[i] != IGN)
+        assert np.allclose(dW0[j], e, atol=1e-13, rtol=0)
+
+
 ALL_PINS = [pin_hand_example, pin_zero_weights, pin_single_class, pin_two_classes,
             pin_equal_rows, pin_translation, pin_rows_sum_to_zero, pin_finite_differences,
-            pin_torch_library, pin_sampled_rows, pin_reduced_loss, pin_rejects_bad_target]
+            pin_torch_library, pin_sampled_rows, pin_reduced_loss, pin_rejects_bad_target,
+            pin_backward]

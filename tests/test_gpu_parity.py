@@ -260,6 +260,47 @@ def test_split_dH_thinned_blocks(pattern, dtype):
 
 
 @pytest.mark.parametrize("dtype", [wl.DTYPE_F32, wl.DTYPE_BF16])
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+def test_invalid_targets_poison(dtype, fused):
+    """The header's contract for a target outside [0, V) that is not
+    ignore_index: that token's loss and dH row are NaN and every element of
+    dW is NaN; its lse and every other token's loss, lse and dH row are those
+    of the same batch with the bad targets ignored; ignored tokens get loss 0
+    and a zero dH row.  Unsharded flce_forward + flce_backward, and the fused
+    call (sum reduction, whose reduced loss is then NaN)."""
+    import linear_cross_entropy_flce_amd as flce
+    T, d, V, g = 300, 64, 1100, 0.25
+    inp = wl.make_inputs(T, d, V, dtype, seed=31, sigma_w=0.4, ignore_frac=0.15)
+    bad = np.array([5, 6, 257])
+    inp.y[bad] = [V + 3, -7, V]
+    H, W, y = device_inputs(inp)
+    plan = flce.flce_plan(T, d, V, dtype)
+    ws = flce.workspace(plan, W.device)
+    if fused:
+        out = flce.flce_forward_backward(plan, H, W, y, IGN, "sum", g, ws=ws)
+        loss, lse, dH, dW, red = (out[k] for k in ("loss", "lse", "dH", "dW", "loss_reduced"))
+    else:
+        red = torch.empty(1, dtype=torch.float32, device=W.device)
+        loss, lse, _ = flce.flce_forward(plan, H, W, y, IGN, g, loss_reduced=red, ws=ws)
+        dH, dW = flce.flce_backward(plan, H, W, y, lse, IGN, g, ws=ws)
+    torch.cuda.synchronize()
+    loss, lse = loss.cpu().numpy(), lse.cpu().numpy()
+    dH, dW = dH.float().cpu().numpy(), dW.cpu().numpy()
+    assert np.all(np.isnan(loss[bad])) and np.all(np.isnan(dH[bad]))
+    assert np.all(np.isnan(dW)) and np.isnan(red.item())
+    ok = np.ones(T, bool)
+    ok[bad] = False
+    ign = inp.y == IGN
+    assert np.all(loss[ign] == 0.0) and np.all(dH[ign] == 0.0)
+    clean = wl.Inputs(inp.H, inp.W, inp.y.copy(), dtype)
+    clean.y[bad] = IGN
+    rl, rs, rdH, _ = oracle.forward_backward(clean.H_f32(), clean.W_f32(), clean.y, IGN, g)
+    assert np.all(np.isfinite(lse)) and max_abs(lse, rs) <= TOL[dtype]["loss"]
+    assert max_abs(loss, rl, ok) <= TOL[dtype]["loss"]
+    assert rel_fro(dH[ok], rdH[ok]) <= TOL[dtype]["grad"]
+
+
+@pytest.mark.parametrize("dtype", [wl.DTYPE_F32, wl.DTYPE_BF16])
 def test_accumulate_dW(dtype):
     inp = wl.make_inputs(300, 48, 700, dtype, seed=19, sigma_w=0.4)
     base = np.random.default_rng(0).standard_normal((700, 48)).astype(np.float32)

@@ -38,6 +38,9 @@ MUTATIONS = {
     "dW_overwrite": ("dW += dZ.T @ H[r0:r1]", "dW = dZ.T @ H[r0:r1]"),
     "dW_wrong_operand": ("dW += dZ.T @ H[r0:r1]", "dW += dZ.T @ H[r0:r1][::-1]"),
     "range_check": ("bad = valid & ((target < 0) | (target >= V))", "bad = valid & (target < 0)"),
+    "backward_swapped": ("    return dH, dW\n", "    return dW, dH\n"),
+    "backward_drops_scale": ("ignore_index, grad_scale, row_chunk)\n    return dH, dW",
+                             "ignore_index, 1.0, row_chunk)\n    return dH, dW"),
 }
 
 
