@@ -367,6 +367,50 @@ def scoring_leg(flce, H, W, y, lse, stream, reps: int = 5):
     return out
 
 
+def forms_leg(flce, wl, plan, H, W, y, ws, stream, reps: int):
+    """The forward alone in its two forms of the target logit: taken from the
+    tile's accumulator (FLCE_TARGET_IN_TILE) and a pure log-sum-exp sweep
+    followed by one gathered dot product per token (FLCE_TARGET_GATHER).
+    Timed with hipEvents on `stream`, the forms interleaved rep by rep."""
+    import torch
+    T = plan.T
+    dev = W.device
+    gplan = type(plan).from_buffer_copy(plan)
+    gplan.target_logit = flce.FLCE_TARGET_GATHER
+    outs = {}
+    loss = torch.empty(T, dtype=torch.float32, device=dev)
+    lse = torch.empty(T, dtype=torch.float32, device=dev)
+    plans = {"in_tile": plan, "gather": gplan}
+    for p in plans.values():
+        flce.flce_forward(p, H, W, y, wl.IGNORE_INDEX, 1.0, loss=loss, lse=lse, ws=ws, stream=stream)
+    torch.cuda.synchronize()
+    ms = {k: [] for k in plans}
+    flce.flce_timing_collect()
+    flce.flce_timing_enable(True)
+    for _ in range(reps):
+        for k, p in plans.items():
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            flce.flce_forward(p, H, W, y, wl.IGNORE_INDEX, 1.0, loss=loss, lse=lse, ws=ws,
+                              stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms[k].append(e0.elapsed_time(e1))
+    flce.flce_timing_enable(False)
+    kt = flce.flce_timing_collect()
+    for k, v in ms.items():
+        v.sort()
+        outs[k] = {"fwd_ms_median": round(v[len(v) // 2], 4), "fwd_ms_min": round(v[0], 4)}
+    if "target_logit" in kt:
+        t = kt["target_logit"]
+        outs["gather"]["target_logit_avg_ms"] = round(t["total_ms"] / t["launches"], 4)
+    log(f"  forward forms: in-tile {outs['in_tile']['fwd_ms_median']:.3f} ms, "
+        f"gather {outs['gather']['fwd_ms_median']:.3f} ms")
+    outs["default"] = "in_tile" if plan.target_logit == flce.FLCE_TARGET_IN_TILE else "gather"
+    return outs
+
+
 def copy_calibration(mib: int):
     """A plain copy of mib MiB (read mib, write mib), three times: the byte
     counters of a profiler run over it give the scale of FETCH_SIZE and
@@ -530,6 +574,7 @@ def main():
     shard = shard_leg(flce, wl, H, W, cfg, ws, stream, args.shard_steps) if args.shard_steps > 0 else None
     scoring = scoring_leg(flce, H, W, y, lse, stream) if args.shard_steps > 0 else None
     fused = fused_leg(flce, wl, plan, H, W, y, ws, stream, args.shard_steps) if args.shard_steps > 0 else None
+    forms = forms_leg(flce, wl, plan, H, W, y, ws, stream, 2 * args.shard_steps + 1) if args.shard_steps > 0 else None
 
     cpu = None
     if args.cpu_rows > 0:
@@ -574,6 +619,7 @@ def main():
         "shard_mode": shard,
         "token_scoring": scoring,
         "fused_call": fused,
+        "target_logit_forms": forms,
         "plan": {"fwd_splits": plan.fwd_splits, "bwd_block": plan.bwd_block,
                  "bwd_slab": plan.bwd_slab, "n_blocks": plan.n_blocks, "n_slabs": plan.n_slabs},
     }

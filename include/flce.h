@@ -33,7 +33,8 @@
  *     thread-local error string.  All work is ordered on `stream` (a
  *     hipStream_t; NULL means the default stream).
  *   - Requirements: T >= 0, V >= 1, d >= 8 and d % 8 == 0, T, V < 2^31,
- *     d <= 65536, H and W each below 2 GiB, device pointers 16-byte aligned.
+ *     d <= 65536, device pointers 16-byte aligned.  H, W and dW may be larger
+ *     than 2 GiB.
  *     Violations are reported before anything is launched.
  *   - Results are bitwise reproducible for identical inputs and plan: every
  *     reduction runs in a fixed order, and no floating-point atomics are used.
@@ -93,8 +94,21 @@ typedef struct flce_plan {
    * chosen block and slab (dH then never splits). */
   uint64_t dh_split_bytes;
   uint32_t magic;          /* set by flce_plan; checked by the other calls */
-  uint32_t reserved;
+  uint32_t target_logit;   /* flce_target_logit_t: how the forward takes each token's
+                              target logit; flce_plan sets the default, and a caller
+                              may change it in its copy of the plan */
 } flce_plan_t;
+
+/* Two forms of the forward's target logit z_{i, y_i}:
+ *   FLCE_TARGET_IN_TILE: each vocab tile's epilogue compares its rows with
+ *     the tokens' targets and keeps the matching fp32 accumulator value; lse
+ *     and z_t then come from the same rounded logits.
+ *   FLCE_TARGET_GATHER: the sweep is a pure log-sum-exp (no per-tile target
+ *     test) and z_t = H[i] . W[y_i] is one gathered dot product per token
+ *     afterwards (Cut Cross-Entropy indexes only the target logit; first
+ *     page, section 3).  Its fp32 sum runs in another order than the tile's,
+ *     so loss may differ from the other form by fp32 rounding of |z|. */
+typedef enum { FLCE_TARGET_IN_TILE = 0, FLCE_TARGET_GATHER = 1 } flce_target_logit_t;
 
 /* flce_plan -- choose tiles, splits, token block and vocab slab.
  * Section 3 of the first page bounds the method's vocab-axis residency by one
@@ -113,7 +127,8 @@ typedef struct flce_plan {
  * Host-only integer arithmetic; launches nothing.  Returns
  * FLCE_ERR_INVALID_ARG for a null `out`, negative/zero sizes or an unknown
  * dtype, FLCE_ERR_UNSUPPORTED for d % 8 != 0 or sizes beyond the limits, and
- * FLCE_ERR_WORKSPACE when the cap cannot hold the smallest token block. */
+ * FLCE_ERR_WORKSPACE when the cap cannot hold the smallest token block.
+ * A vocab slab's rows of W (bwd_slab x d elements) are kept below 2^31 bytes. */
 flce_status_t flce_plan(int64_t T, int64_t d, int64_t V, flce_dtype_t dtype,
                         uint64_t vocab_ws_cap_bytes, flce_plan_t* out);
 
@@ -124,7 +139,8 @@ flce_status_t flce_plan(int64_t T, int64_t d, int64_t V, flce_dtype_t dtype,
  *   loss_reduced : NULL, or a device float that receives scale * sum(loss)
  *             (summed in a fixed order, in double precision).
  *   ws, ws_bytes : caller workspace of at least plan->fwd_ws_bytes.
- * T == 0 is valid and writes only loss_reduced (= 0). */
+ * The target logit is taken as plan->target_logit says (FLCE_ERR_INVALID_ARG
+ * for another value).  T == 0 is valid and writes only loss_reduced (= 0). */
 flce_status_t flce_forward(const flce_plan_t* plan, const void* H, const void* W,
                            const int64_t* y, int64_t ignore_index, float scale, float* loss,
                            float* lse, float* loss_reduced, void* ws, uint64_t ws_bytes,

@@ -23,6 +23,8 @@ FLCE_ERR_WORKSPACE = -3
 FLCE_ERR_HIP = -4
 FLCE_REDUCE_SUM = 0
 FLCE_REDUCE_MEAN_VALID = 1
+FLCE_TARGET_IN_TILE = 0
+FLCE_TARGET_GATHER = 1
 
 EXPORTED = ["flce_plan", "flce_forward", "flce_backward", "flce_forward_backward",
             "flce_forward_shard",
@@ -43,7 +45,7 @@ class Plan(ctypes.Structure):
         ("dh_acc_bytes", ctypes.c_uint64), ("bwd_ws_bytes", ctypes.c_uint64),
         ("ws_bytes", ctypes.c_uint64), ("vocab_ws_cap", ctypes.c_uint64),
         ("naive_logits_bytes", ctypes.c_uint64), ("dh_split_bytes", ctypes.c_uint64),
-        ("magic", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+        ("magic", ctypes.c_uint32), ("target_logit", ctypes.c_uint32),
     ]
 
     def as_dict(self):

@@ -3,7 +3,7 @@
 // Host-only code.  Nothing here allocates device memory or synchronises; every
 // launch goes to the caller's stream in a fixed order, so results are
 // reproducible bit for bit.
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -67,11 +67,12 @@ flce_status_t hip_fail(hipError_t e, const char* what) {
 // ------------------------------------------------------------ kernel timing
 enum KernelId {
   K_FWD_SWEEP, K_FWD_MERGE, K_LOSS_SUM, K_BWD_DZ, K_BWD_DHDW, K_DH_REDUCE, K_FILL,
-  K_SHARD_MERGE, K_TOKEN_LOGIT, K_CAST, K_TRANSPOSE, K_COMPACT, K_COUNT
+  K_SHARD_MERGE, K_TOKEN_LOGIT, K_CAST, K_TRANSPOSE, K_COMPACT, K_TARGET_LOGIT, K_COUNT
 };
 const char* const kKernelNames[K_COUNT] = {
-    "fwd_sweep", "fwd_merge",   "loss_sum",  "bwd_dz",   "bwd_dhdw", "dh_reduce",
-    "fill_zero", "shard_merge", "token_logit", "cast_bf16", "gather_h", "compact"};
+    "fwd_sweep", "fwd_merge",   "loss_sum",    "bwd_dz",    "bwd_dhdw", "dh_reduce",
+    "fill_zero", "shard_merge", "token_logit", "cast_bf16", "gather_h", "compact",
+    "target_logit"};
 
 struct TimingRec {
   int kid;
@@ -144,26 +145,36 @@ double backward_cost(int64_t T, int64_t d, int64_t V, int64_t B, int64_t Vs,
                      const flce::TileInfo& ti, bool dh_split) {
   const double unit = 256.0 * 256.0 * 256.0;
   const int64_t n_dt_h = cdiv(d, ti.dh_bn), n_dt_w = cdiv(d, ti.dw_bm);
+  // one (block, slab) launch pair of tc tokens and vc vocab rows
+  auto pair = [&](int64_t tc, int64_t vc, bool first_block) {
+    const int64_t dz_tiles = cdiv(vc, ti.logit_bm) * cdiv(tc, ti.logit_bn);
+    const int64_t dh_tiles = cdiv(tc, ti.dh_bm) * n_dt_h;
+    const int64_t dw_tiles = cdiv(vc, ti.dw_bn) * n_dt_w;
+    const double dz_tile = (double)ti.logit_bm * ti.logit_bn * d / unit;
+    const double dh_tile = (double)ti.dh_bm * ti.dh_bn * vc / unit;
+    const double dw_tile = (double)ti.dw_bm * ti.dw_bn * tc / unit;
+    double c = cdiv(dz_tiles, kComputeUnits) * dz_tile * 1.10;
+    const int64_t dh_parts =
+        dh_split && 2 * dh_tiles <= kComputeUnits
+            ? std::min<int64_t>(kComputeUnits / dh_tiles, cdiv(vc, ti.dh_bk))
+            : 1;
+    c += cdiv(dh_tiles, kComputeUnits) * (dh_tile / dh_parts + 0.5);
+    c += cdiv(dw_tiles, kComputeUnits) * dw_tile * (first_block ? 1.035 : 1.07);
+    return c;
+  };
+  // a block sweeps full slabs and one possibly shorter last slab
+  const int64_t n_full_s = V / Vs, last_s = V - n_full_s * Vs;
+  auto block = [&](int64_t tc, bool first_block) {
+    double c = (double)n_full_s * pair(tc, Vs, first_block);
+    if (last_s > 0) c += pair(tc, last_s, first_block);
+    return c;
+  };
+  // blocks: the first, the other full ones, and a shorter last one; the sum
+  // is the same as walking them one by one, in O(1)
+  const int64_t n_full_b = T / B, last_b = T - n_full_b * B;
   double cost = 0;
-  for (int64_t t0 = 0; t0 < T; t0 += B) {
-    const int64_t tc = T - t0 < B ? T - t0 : B;
-    for (int64_t v0 = 0; v0 < V; v0 += Vs) {
-      const int64_t vc = V - v0 < Vs ? V - v0 : Vs;
-      const int64_t dz_tiles = cdiv(vc, ti.logit_bm) * cdiv(tc, ti.logit_bn);
-      const int64_t dh_tiles = cdiv(tc, ti.dh_bm) * n_dt_h;
-      const int64_t dw_tiles = cdiv(vc, ti.dw_bn) * n_dt_w;
-      const double dz_tile = (double)ti.logit_bm * ti.logit_bn * d / unit;
-      const double dh_tile = (double)ti.dh_bm * ti.dh_bn * vc / unit;
-      const double dw_tile = (double)ti.dw_bm * ti.dw_bn * tc / unit;
-      cost += cdiv(dz_tiles, kComputeUnits) * dz_tile * 1.10;
-      const int64_t dh_parts =
-          dh_split && 2 * dh_tiles <= kComputeUnits
-              ? std::min<int64_t>(kComputeUnits / dh_tiles, cdiv(vc, ti.dh_bk))
-              : 1;
-      cost += cdiv(dh_tiles, kComputeUnits) * (dh_tile / dh_parts + 0.5);
-      cost += cdiv(dw_tiles, kComputeUnits) * dw_tile * (t0 > 0 ? 1.07 : 1.035);
-    }
-  }
+  if (n_full_b > 0) cost += block(B, true) + (double)(n_full_b - 1) * block(B, false);
+  if (last_b > 0) cost += block(last_b, n_full_b == 0);
   return cost;
 }
 
@@ -224,7 +235,10 @@ flce_status_t forward_impl(const flce_plan_t* plan, const void* H, const void* W
   if (p.T > 0 && ws_bytes < p.fwd_ws_bytes)
     return fail(FLCE_ERR_WORKSPACE, "forward needs %llu workspace bytes, got %llu",
                 (unsigned long long)p.fwd_ws_bytes, (unsigned long long)ws_bytes);
+  if (p.target_logit != FLCE_TARGET_IN_TILE && p.target_logit != FLCE_TARGET_GATHER)
+    return fail(FLCE_ERR_INVALID_ARG, "unknown target_logit mode %u", (unsigned)p.target_logit);
   const bool bf16 = p.dtype == FLCE_BF16;
+  const bool capture = p.target_logit == FLCE_TARGET_IN_TILE;
   hipError_t e;
   if (p.T == 0) {
     if (loss_reduced) {
@@ -258,9 +272,16 @@ flce_status_t forward_impl(const flce_plan_t* plan, const void* H, const void* W
   const double esz = (double)p.elem_bytes;
   Timed t_sweep(s, K_FWD_SWEEP, 2.0 * p.T * p.d * p.V,
                 (p.T + p.V) * p.d * esz + (double)p.fwd_splits * p.T * 8 + p.T * 12.0);
-  e = flce::launch_fwd_sweep(a, bf16, (int)grid, s);
+  e = flce::launch_fwd_sweep(a, bf16, capture, (int)grid, s);
   t_sweep.done();
   if (e != hipSuccess) return hip_fail(e, "forward sweep launch");
+  if (!capture) {
+    // the target logits as gathered dot products (H row + W row per token)
+    Timed tm(s, K_TARGET_LOGIT, 0, 2.0 * p.T * p.d * esz + p.T * 12.0);
+    e = flce::launch_target_logit(a, bf16, s);
+    tm.done();
+    if (e != hipSuccess) return hip_fail(e, "target logit launch");
+  }
   flce::MergeArgs m;
   m.part = part;
   m.zt = zt;
@@ -499,11 +520,15 @@ flce_status_t flce_plan(int64_t T, int64_t d, int64_t V, flce_dtype_t dtype, uin
 
   const bool bf16 = dtype == FLCE_BF16;
   const int64_t esz = bf16 ? 2 : 4;
-  // the kernels address H and W through buffer resources with 32-bit offsets
-  if (T * d * esz >= (1ll << 31) || V * d * esz >= (1ll << 31))
-    return fail(FLCE_ERR_UNSUPPORTED, "H (%lld bytes) and W (%lld bytes) must each be below 2 GiB",
-                (long long)(T * d * esz), (long long)(V * d * esz));
   const flce::TileInfo ti = flce::tile_info(bf16);
+  // The kernels address their operands through buffer resources with 32-bit
+  // byte offsets, each based at the first row of the tile (or, for dH's W
+  // operand, of the vocab slab) it reads, so H and W may exceed 2 GiB; a
+  // slab's W rows must stay below 2^31 bytes.
+  const int64_t slab_rows_max = ((1ll << 31) - 1) / (d * esz) / ti.logit_bm * ti.logit_bm;
+  if (slab_rows_max < ti.logit_bm)
+    return fail(FLCE_ERR_UNSUPPORTED, "d = %lld is too large for a %d-row vocab tile",
+                (long long)d, ti.logit_bm);
   if (cap == 0) cap = kDefaultCap;
   // tile offsets into the workspace are 32-bit: keep it below 2 GiB
   if (cap > kMaxCap) cap = kMaxCap;
@@ -552,7 +577,7 @@ flce_status_t flce_plan(int64_t T, int64_t d, int64_t V, flce_dtype_t dtype, uin
       const uint64_t reserve =
           pass == 0 && 2 * cdiv(B, ti.dh_bm) * dh_nt <= flce::dh_split_slots() ? split : 0;
       double best_cost = 0;
-      for (int64_t Vs = ti.logit_bm; Vs <= Vfull; Vs += ti.logit_bm) {
+      for (int64_t Vs = ti.logit_bm; Vs <= Vfull && Vs <= slab_rows_max; Vs += ti.logit_bm) {
         const int64_t slabs = cdiv(V, Vs);
         const uint64_t need = (uint64_t)(B * Vs * esz) +
                               (slabs > 1 ? (uint64_t)(B * d * 4) : 0) +

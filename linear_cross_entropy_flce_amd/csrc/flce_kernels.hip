@@ -169,7 +169,7 @@ __device__ __forceinline__ int target_code(const Targets& g, int64_t t, int V) {
 // that the 32 workgroups an XCD holds at once are `grp` token tiles x `spl`
 // splits: they share H panels within a token tile and W panels across the
 // token tiles, in that XCD's L2.
-template <typename E>
+template <typename E, bool CAPTURE>
 __global__ void __launch_bounds__(LogitCfg<E>::T::NT, 1)
     fwd_sweep_kernel(FwdArgs a) {
   using TL = typename LogitCfg<E>::T;
@@ -193,14 +193,16 @@ __global__ void __launch_bounds__(LogitCfg<E>::T::NT, 1)
   const int wm = wave / TL::WN, wn = wave % TL::WN;
   const int64_t t0 = (int64_t)tt * TL::BN;
 
-  // B operand: H rows of this token tile (K-contiguous).
-  const __amdgpu_buffer_rsrc_t rsH = make_rsrc(a.H, clamp_bytes(a.T * a.d * ESZ));
-  const __amdgpu_buffer_rsrc_t rsW = make_rsrc(a.W, clamp_bytes((int64_t)a.V * a.d * ESZ));
+  // B operand: H rows of this token tile (K-contiguous).  Each operand tile
+  // gets a buffer resource based at its own first row, so H and W may exceed
+  // the 2^31 bytes that 32-bit buffer offsets reach: only a tile (at most
+  // 256 rows x 65,536 elements) has to lie below that.
   Operand B;
-  B.rs = rsH;
-  B.off = (uint32_t)(t0 * a.d * ESZ);
-  B.ld_bytes = (uint32_t)(a.d * ESZ);
   B.rows = (int)min<int64_t>(TL::BN, a.T - t0);
+  B.rs = make_rsrc(reinterpret_cast<const char*>(a.H) + t0 * a.d * ESZ,
+                   (uint32_t)((int64_t)B.rows * a.d * ESZ));
+  B.off = 0;
+  B.ld_bytes = (uint32_t)(a.d * ESZ);
   B.cols = a.d;
 
   // Per-lane state for its NI token columns: running max and sum over the
@@ -212,18 +214,19 @@ __global__ void __launch_bounds__(LogitCfg<E>::T::NT, 1)
     m_run[j] = kNegInf;
     s_run[j] = 0.f;
     const int64_t t = t0 + TL::col_of(wn, j);
-    tgt[j] = t < a.T ? target_code(a.tg, t, a.V) : kIgnored;
+    tgt[j] = CAPTURE && t < a.T ? target_code(a.tg, t, a.V) : kIgnored;
   }
 
   TL tile;
   Operand A;
-  A.rs = rsW;
+  A.off = 0;
   A.ld_bytes = (uint32_t)(a.d * ESZ);
   A.cols = a.d;
   for (int vt = vt_begin; vt < vt_end; ++vt) {
     const int64_t v0 = (int64_t)vt * TL::BM;
-    A.off = (uint32_t)(v0 * a.d * ESZ);
     A.rows = (int)min<int64_t>(TL::BM, a.V - v0);
+    A.rs = make_rsrc(reinterpret_cast<const char*>(a.W) + v0 * a.d * ESZ,
+                     (uint32_t)((int64_t)A.rows * a.d * ESZ));
     tile.zero();
     tile.mainloop(A, B, a.d, lds);
 
@@ -259,9 +262,11 @@ __global__ void __launch_bounds__(LogitCfg<E>::T::NT, 1)
         s_run[j] = s_run[j] * fast_exp2((m_run[j] - m_new) * kLog2e) + sum;
         m_run[j] = m_new;
       }
-      // target logit, taken from the fp32 accumulator (rare: one tile per token)
+      // target logit, taken from the fp32 accumulator (rare: one tile per
+      // token); without CAPTURE the sweep is a pure log-sum-exp and the
+      // target logits come from a gathered dot product afterwards
       const int rt = tgt[j] - wrow0 - 4 * (lane >> 5);
-      if (tgt[j] >= wrow0 && tgt[j] < wrow0 + TL::WTM) {
+      if (CAPTURE && tgt[j] >= wrow0 && tgt[j] < wrow0 + TL::WTM) {
         float zt = 0.f;
         bool hit = false;
 #pragma unroll
@@ -505,10 +510,11 @@ __device__ __forceinline__ void dz_tile(const DzArgs& a, int tm, int tn, char* l
   if (tl0 >= t_count) return;
 
   Operand A, B;
-  A.rs = make_rsrc(a.W, clamp_bytes((int64_t)a.V * a.d * ESZ));
-  A.off = (uint32_t)(v0 * a.d * ESZ);
-  A.ld_bytes = (uint32_t)(a.d * ESZ);
   A.rows = (int)max<int64_t>(0, min<int64_t>(TL::BM, a.V - v0));
+  A.rs = make_rsrc(reinterpret_cast<const char*>(a.W) + v0 * a.d * ESZ,
+                   (uint32_t)((int64_t)A.rows * a.d * ESZ));  // W may pass 2^31 bytes
+  A.off = 0;
+  A.ld_bytes = (uint32_t)(a.d * ESZ);
   A.cols = a.d;
   B.rs = make_rsrc(a.Hc, clamp_bytes((int64_t)a.blk.t_max * a.d * ESZ));
   B.off = (uint32_t)(tl0 * a.d * ESZ);
@@ -689,8 +695,12 @@ __device__ __forceinline__ void dh_body(const DhArgs& a, int bid, char* lds) {
   A.ld_bytes = (uint32_t)(a.ldz * ESZ);
   A.rows = (int)min<int64_t>(TL::BM, t_count - tl0);
   A.cols = K;
-  B.rs = make_rsrc(a.W, clamp_bytes((int64_t)a.V * a.d * ESZ));
-  B.off = (uint32_t)(((a.v_begin + k_lo) * a.d + n0) * ESZ);
+  // W rows of this part of the slab, based at the part's first row: the
+  // planner keeps a slab's rows (K x d elements) below 2^31 bytes, so W
+  // itself may be larger
+  B.rs = make_rsrc(reinterpret_cast<const char*>(a.W) + (a.v_begin + k_lo) * a.d * ESZ,
+                   clamp_bytes((int64_t)K * a.d * ESZ));
+  B.off = (uint32_t)(n0 * ESZ);
   B.ld_bytes = (uint32_t)(a.d * ESZ);
   B.rows = K;
   B.cols = (int)min<int64_t>(TL::BN, a.d - n0);
@@ -1064,6 +1074,37 @@ __global__ void __launch_bounds__(256) token_logit_kernel(TokenArgs a) {
   }
 }
 
+// Target logits of the forward when its sweep is a pure log-sum-exp: one
+// wave per token, zt[t] = H[t] . W[y_t - start] (fp32 products of the stored
+// values, each lane's chunks in ascending order, then a fixed xor tree) for
+// targets inside this vocab range; -inf for every other token (ignored,
+// invalid, or held by another shard), which the merge never reads as a logit.
+template <typename E>
+__global__ void __launch_bounds__(256) target_logit_kernel(FwdArgs a) {
+  constexpr int CW = 16 / (int)sizeof(E);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  if (t >= a.T) return;
+  const int code = target_code(a.tg, t, a.V);
+  if (code < 0) {
+    if (lane == 0) a.zt[t] = kNegInf;
+    return;
+  }
+  const char* h = reinterpret_cast<const char*>(a.H) + t * a.d * (int64_t)sizeof(E);
+  const char* w = reinterpret_cast<const char*>(a.W) + (int64_t)code * a.d * (int64_t)sizeof(E);
+  const int nc = a.d / CW;
+  float acc = 0.f;
+#pragma unroll 4
+  for (int c = lane; c < nc; c += 64) {
+    const u32x4_t hv = *reinterpret_cast<const u32x4_t*>(h + (int64_t)c * 16);
+    const u32x4_t wv = *reinterpret_cast<const u32x4_t*>(w + (int64_t)c * 16);
+    acc = dot16(hv, wv, acc, (E*)nullptr);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if (lane == 0) a.zt[t] = acc;
+}
+
 // ================================================================== launchers
 template <typename K, typename Args>
 static hipError_t launch(K kernel, int grid, int threads, int lds, hipStream_t s, const Args& args) {
@@ -1078,17 +1119,23 @@ static hipError_t set_lds(K kernel, int bytes) {
                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
-hipError_t launch_fwd_sweep(const FwdArgs& a, bool bf16, int grid, hipStream_t s) {
-  if (bf16) {
-    using TL = LogitCfg<__bf16>::T;
-    hipError_t e = set_lds(fwd_sweep_kernel<__bf16>, TL::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    return launch(fwd_sweep_kernel<__bf16>, grid, TL::NT, TL::LDS_BYTES, s, a);
-  }
-  using TL = LogitCfg<float>::T;
-  hipError_t e = set_lds(fwd_sweep_kernel<float>, TL::LDS_BYTES);
+template <typename E, bool CAPTURE>
+static hipError_t launch_sweep(const FwdArgs& a, int grid, hipStream_t s) {
+  using TL = typename LogitCfg<E>::T;
+  hipError_t e = set_lds(fwd_sweep_kernel<E, CAPTURE>, TL::LDS_BYTES);
   if (e != hipSuccess) return e;
-  return launch(fwd_sweep_kernel<float>, grid, TL::NT, TL::LDS_BYTES, s, a);
+  return launch(fwd_sweep_kernel<E, CAPTURE>, grid, TL::NT, TL::LDS_BYTES, s, a);
+}
+
+hipError_t launch_fwd_sweep(const FwdArgs& a, bool bf16, bool capture, int grid, hipStream_t s) {
+  if (bf16) return capture ? launch_sweep<__bf16, true>(a, grid, s) : launch_sweep<__bf16, false>(a, grid, s);
+  return capture ? launch_sweep<float, true>(a, grid, s) : launch_sweep<float, false>(a, grid, s);
+}
+
+hipError_t launch_target_logit(const FwdArgs& a, bool bf16, hipStream_t s) {
+  const int grid = (int)((a.T + 3) / 4);
+  if (bf16) return launch(target_logit_kernel<__bf16>, grid, 256, 0, s, a);
+  return launch(target_logit_kernel<float>, grid, 256, 0, s, a);
 }
 
 hipError_t launch_fwd_merge(const MergeArgs& a, hipStream_t s) {

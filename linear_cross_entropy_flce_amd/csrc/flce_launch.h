@@ -2,7 +2,7 @@
 // and the kernels (flce_kernels.hip).  Not part of the public C-ABI.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
 namespace flce {
@@ -120,7 +120,11 @@ struct TileInfo {
 };
 
 TileInfo tile_info(bool bf16);
-hipError_t launch_fwd_sweep(const FwdArgs& a, bool bf16, int grid, hipStream_t s);
+// The forward sweep.  capture: the target logit is taken from the tile's fp32
+// accumulator into a.zt; otherwise the sweep is a pure log-sum-exp and
+// launch_target_logit fills a.zt with gathered dot products.
+hipError_t launch_fwd_sweep(const FwdArgs& a, bool bf16, bool capture, int grid, hipStream_t s);
+hipError_t launch_target_logit(const FwdArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_fwd_merge(const MergeArgs& a, hipStream_t s);
 // Reduced loss and the matching gradient scale (see loss_reduce_kernel).
 struct ReduceArgs {

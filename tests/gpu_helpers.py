@@ -34,9 +34,20 @@ def device_inputs(inp: wl.Inputs):
     return H, W, y
 
 
+def gather_plan(plan):
+    """A copy of the plan whose forward takes the target logit as a gathered
+    dot product (pure log-sum-exp sweep)."""
+    p = type(plan).from_buffer_copy(plan)
+    p.target_logit = flce.FLCE_TARGET_GATHER
+    return p
+
+
 def run_gpu(inp: wl.Inputs, loss_scale=1.0, grad_scale=1.0, cap=0, backward=True, dev=None,
-            accumulate_dW=False, dW_init=None):
-    """One forward (+ backward) through the C-ABI.  Returns numpy results."""
+            accumulate_dW=False, dW_init=None, gather=True):
+    """One forward (+ backward) through the C-ABI.  Returns numpy results.
+
+    With `gather`, the forward also runs a second time with the target logit
+    gathered by index (loss_gather, lse_gather, red_gather)."""
     H, W, y = dev if dev is not None else device_inputs(inp)
     plan = flce.flce_plan(inp.T, inp.d, inp.V, inp.dtype, cap)
     ws = flce.workspace(plan, W.device)
@@ -44,6 +55,11 @@ def run_gpu(inp: wl.Inputs, loss_scale=1.0, grad_scale=1.0, cap=0, backward=True
     loss, lse, _ = flce.flce_forward(plan, H, W, y, inp.ignore_index, loss_scale,
                                      loss_reduced=red, ws=ws)
     out = dict(plan=plan, loss=loss, lse=lse, red=red)
+    if gather:
+        gred = torch.empty(1, dtype=torch.float32, device=W.device)
+        gl, gs, _ = flce.flce_forward(gather_plan(plan), H, W, y, inp.ignore_index, loss_scale,
+                                      loss_reduced=gred, ws=ws)
+        out.update(loss_gather=gl, lse_gather=gs, red_gather=gred)
     if backward:
         dW = None
         if dW_init is not None:
@@ -83,8 +99,12 @@ def logit_tol(dtype, d, zmax):
 
 
 def compare(got, ref, dtype, what=("loss", "lse", "dH", "dW"), rows=None, loss_tol=None,
-            grad_tol=None):
-    """Asserts the tolerances; returns the error figures."""
+            grad_tol=None, gather_tol=None):
+    """Asserts the tolerances; returns the error figures.
+
+    When `got` holds the gathered-target forward's loss and lse too, they are
+    held to the same loss tolerance, widened for fp32 to `gather_tol` if given
+    (the gathered fp32 dot product sums in another order than the tile)."""
     tol = dict(TOL[dtype])
     if loss_tol is not None:
         tol["loss"] = loss_tol
@@ -107,6 +127,21 @@ def compare(got, ref, dtype, what=("loss", "lse", "dH", "dW"), rows=None, loss_t
     if "dW" in what:
         errs["dW"] = rel_fro(got["dW"], ref["dW"])
         assert errs["dW"] <= tol["grad"], errs
+    if "loss_gather" in got:
+        if gather_tol is None and dtype == wl.DTYPE_F32 and np.ndim(got.get("dH")) == 2:
+            # |z_t| = |lse - loss|: the gathered fp32 dot product carries about
+            # sqrt(d) ulps of it (logit_tol), like any fp32 sum of d products
+            zt = np.abs(np.asarray(lse_ref, np.float64) - np.asarray(loss_ref, np.float64))
+            zmax = float(max(np.abs(lse_ref).max(initial=0.0), zt.max(initial=0.0)))
+            gather_tol = logit_tol(dtype, got["dH"].shape[1], zmax)
+        gt = tol["loss"] if gather_tol is None else max(tol["loss"], gather_tol)
+        # both forms run the same log-sum-exp arithmetic: identical lse bits
+        assert np.array_equal(got["lse_gather"], got["lse"]), "lse differs between the forms"
+        for k, r in (("loss", loss_ref), ("lse", lse_ref)):
+            if k in what:
+                g = got[k + "_gather"] if rows is None else got[k + "_gather"][rows]
+                errs[k + "_gather"] = max_abs(g, r)
+                assert errs[k + "_gather"] <= gt, errs
     return errs
 
 

@@ -77,13 +77,29 @@ def test_version_and_status_strings(lib):
     ((10, 12, 1000, 1), flce.FLCE_ERR_UNSUPPORTED),
     ((10, 65544, 1000, 1), flce.FLCE_ERR_UNSUPPORTED),
     ((1 << 31, 128, 1000, 1), flce.FLCE_ERR_UNSUPPORTED),
-    ((1 << 20, 1024, 1000, 1), flce.FLCE_ERR_UNSUPPORTED),   # H of 2 GiB
-    ((1000, 4096, 1 << 18, 0), flce.FLCE_ERR_UNSUPPORTED),   # fp32 W of 4 GiB
+    ((10, 128, 1 << 31, 1), flce.FLCE_ERR_UNSUPPORTED),
 ])
 def test_plan_rejects(lib, args, status):
     st, _ = flce.flce_plan_status(*args)
     assert st == status
     assert flce.last_error()
+
+
+@pytest.mark.parametrize("T,d,V,dt", [
+    (1 << 20, 1024, 1000, flce.FLCE_BF16),      # H of 2 GiB
+    (1000, 4096, 1 << 18, flce.FLCE_F32),       # fp32 W of 4 GiB
+    (384, 8192, 131200, flce.FLCE_BF16),        # bf16 W of 2.15 GB
+    (4096, 65536, 50000, flce.FLCE_BF16),       # the widest hidden size
+    (200_000_000, 8, 3, flce.FLCE_F32),         # 6.4 GB of fp32 H (the token order fills the cap)
+])
+def test_plan_accepts_operands_beyond_2GiB(lib, T, d, V, dt):
+    """H and W may exceed 2^31 bytes (each kernel tile has its own base);
+    a vocab slab's rows of W, which dH addresses from one base, stay below."""
+    st, p = flce.flce_plan_status(T, d, V, dt)
+    assert st == flce.FLCE_OK, flce.last_error()
+    esz = 2 if dt == flce.FLCE_BF16 else 4
+    assert p.bwd_slab * d * esz < 2 ** 31
+    assert p.n_slabs * p.bwd_slab >= V and p.bwd_ws_bytes <= p.vocab_ws_cap
 
 
 def test_plan_accepts_dW_beyond_2GiB(lib):

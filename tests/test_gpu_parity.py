@@ -142,6 +142,10 @@ def test_large_logits_running_max():
         tl = TOL[dtype]["loss"] + 4 * ulp
         assert max_abs(got["loss"], ref["loss"]) <= tl
         assert max_abs(got["lse"], ref["lse"]) <= tl
+        # the gathered target logit (pure log-sum-exp sweep) sums its 64
+        # products in another order: sqrt(d) more ulps of |z| in fp32
+        assert np.array_equal(got["lse_gather"], got["lse"])
+        assert max_abs(got["loss_gather"], ref["loss"]) <= tl + np.sqrt(64) * ulp
         # the same absolute error in z - lse is a relative error of every
         # softmax entry, hence of dZ
         tg = TOL[dtype]["grad"] + 8 * ulp
@@ -386,6 +390,55 @@ def test_dW_beyond_2GiB():
     tail = rel_fro(got["dW"][first:], ref["dW"][first:])
     log("  errors", errs, f"dW rows {first}..{V - 1}: {tail:.3e}")
     assert tail <= TOL[wl.DTYPE_BF16]["grad"]
+
+
+@pytest.mark.timeout(900)
+def test_W_beyond_2GiB():
+    """An LM head whose bf16 W (131,200 x 8,192 x 2 bytes = 2.15 GB) is
+    larger than the 2^31 bytes a 32-bit buffer offset reaches: the kernels
+    address each W tile (and dH each vocab slab) from its own first row.
+    Every output against the oracle, and the rows of W that lie past 2^31
+    bytes on their own (their loss gradient dW rows)."""
+    T, d, V = 384, 8192, 131200
+    log(f"W beyond 2 GiB: T={T} d={d} V={V} bf16")
+    inp = wl.make_inputs(T, d, V, wl.DTYPE_BF16, seed=4343, sigma_w=0.02, ignore_frac=0.1)
+    assert V * d * 2 > 2 ** 31
+    # targets in the rows past 2^31 bytes for a third of the tokens
+    first = (1 << 31) // (d * 2)
+    inp.y[::3] = np.where(inp.y[::3] == IGN, IGN, first + np.arange(len(inp.y[::3])) % (V - first))
+    g = 1.0 / T
+    got = run_gpu(inp, loss_scale=g, grad_scale=g)
+    assert got["plan"].n_slabs >= 2 and got["plan"].bwd_slab * d * 2 < 2 ** 31
+    log("  oracle")
+    ref = _ref(inp, g)
+    errs = compare(got, ref, wl.DTYPE_BF16)
+    tail = rel_fro(got["dW"][first:], ref["dW"][first:])
+    log("  errors", errs, f"dW rows {first}..{V - 1}: {tail:.3e}")
+    assert tail <= TOL[wl.DTYPE_BF16]["grad"]
+
+
+@pytest.mark.timeout(900)
+def test_H_beyond_2GiB():
+    """131,100 tokens of d = 8,192 in bf16: H is 2.15 GB, past 2^31 bytes;
+    each forward token tile is addressed from its own first row (the
+    backward gathers its token blocks with 64-bit addresses).  Every output
+    against the oracle, and the token rows past 2^31 bytes on their own."""
+    T, d, V = 131100, 8192, 1000
+    log(f"H beyond 2 GiB: T={T} d={d} V={V} bf16")
+    inp = wl.make_inputs(T, d, V, wl.DTYPE_BF16, seed=4444, sigma_w=0.02, ignore_frac=0.1)
+    assert T * d * 2 > 2 ** 31
+    got = run_gpu(inp, grad_scale=1.0 / T)
+    log("  oracle")
+    ref = _ref(inp, 1.0 / T)
+    errs = compare(got, ref, wl.DTYPE_BF16)
+    first = (1 << 31) // (d * 2)
+    tail = dict(loss=max_abs(got["loss"][first:], ref["loss"][first:]),
+                loss_gather=max_abs(got["loss_gather"][first:], ref["loss"][first:]),
+                dH=rel_fro(got["dH"][first:], ref["dH"][first:]))
+    log("  errors", errs, f"rows {first}..{T - 1}:", tail)
+    assert tail["loss"] <= TOL[wl.DTYPE_BF16]["loss"]
+    assert tail["loss_gather"] <= TOL[wl.DTYPE_BF16]["loss"]
+    assert tail["dH"] <= TOL[wl.DTYPE_BF16]["grad"]
 
 
 @pytest.mark.timeout(900)
