@@ -195,6 +195,33 @@ flce_status_t flce_forward_backward(const flce_plan_t* plan, const void* H, cons
                                     int accumulate_dW, void* dW_bf16, void* ws, uint64_t ws_bytes,
                                     void* stream);
 
+/* ---- allocation-free variant ---------------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * flce_forward_backward_scratch is flce_forward_backward with the library's
+ * own static scratch array of FLCE_SCRATCH_BYTES as the workspace: a
+ * file-scope device array that every GPU running the library holds until the
+ * process ends.  The caller passes inputs and outputs only.  The plan must
+ * fit: plan->ws_bytes <= FLCE_SCRATCH_BYTES, which flce_plan() guarantees
+ * with vocab_ws_cap_bytes = FLCE_SCRATCH_BYTES - 256 unless the forward's
+ * per-token partials alone exceed it (T of several million); otherwise
+ * FLCE_ERR_WORKSPACE, before anything is launched.  The first call on a
+ * device looks up the array's device address (FLCE_ERR_HIP if that fails)
+ * and keeps it; no call allocates, frees or copies memory: it only launches
+ * kernels on `stream`.  The array keeps the last call's contents; every byte
+ * a call reads is written earlier in the same call.  Calls that overlap on
+ * one GPU (other streams, other threads) share the array and race: the
+ * caller serialises them.  Kernel timing (flce_timing_enable) does not
+ * record these calls.  Results are bit for bit those of
+ * flce_forward_backward with the same plan and arguments. */
+#define FLCE_SCRATCH_BYTES 268435456ull
+flce_status_t flce_forward_backward_scratch(const flce_plan_t* plan, const void* H,
+                                            const void* W, const int64_t* y, int64_t ignore_index,
+                                            flce_reduction_t reduction, float scale, float* loss,
+                                            float* lse, float* loss_reduced, void* dH, float* dW,
+                                            int accumulate_dW, void* dW_bf16, void* stream);
+
 /* ---- vocab-parallel shard mode ------------------------------------------
  * The Megatron-Lite / bumblebee write-up (section 2.3, step 1) runs this loss
  * vocab-parallel: each of P tensor-parallel ranks holds a contiguous slice of

@@ -25,8 +25,11 @@ FLCE_REDUCE_SUM = 0
 FLCE_REDUCE_MEAN_VALID = 1
 FLCE_TARGET_IN_TILE = 0
 FLCE_TARGET_GATHER = 1
+# bytes of the library's static scratch array (FLCE_SCRATCH_BYTES in flce.h)
+FLCE_SCRATCH_BYTES = 268435456
 
 EXPORTED = ["flce_plan", "flce_forward", "flce_backward", "flce_forward_backward",
+            "flce_forward_backward_scratch",
             "flce_forward_shard",
             "flce_merge_shards", "flce_backward_shard", "flce_token_logprobs", "flce_timing_enable",
             "flce_timing_collect", "flce_status_string", "flce_last_error", "flce_version"]
@@ -88,6 +91,9 @@ def load(path: str = LIB_PATH):
     lib.flce_forward_backward.argtypes = [P, vp, vp, vp, i64, ctypes.c_int, f32, vp, vp, vp, vp,
                                           vp, ctypes.c_int, vp, vp, u64, vp]
     lib.flce_forward_backward.restype = ctypes.c_int
+    lib.flce_forward_backward_scratch.argtypes = [P, vp, vp, vp, i64, ctypes.c_int, f32, vp, vp,
+                                                  vp, vp, vp, ctypes.c_int, vp, vp]
+    lib.flce_forward_backward_scratch.restype = ctypes.c_int
     lib.flce_forward_shard.argtypes = [P, vp, vp, vp, i64, i64, i64, vp, vp, vp, u64, vp]
     lib.flce_forward_shard.restype = ctypes.c_int
     lib.flce_merge_shards.argtypes = [i64, ctypes.c_int32, vp, vp, vp, i64, i64, f32, vp, vp, vp,
@@ -419,3 +425,32 @@ def flce_forward_backward(plan: Plan, H, W, y, ignore_index: int = -100, reducti
                                         _ptr(ws), int(ws.numel() * ws.element_size()),
                                         _stream(stream)))
     return dict(loss=loss, lse=lse, loss_reduced=loss_reduced, dH=dH, dW=dW, dW_bf16=dW_bf16)
+
+
+def flce_forward_backward_scratch(plan: Plan, H, W, y, ignore_index: int, reduction: str,
+                                  scale: float, loss, lse, loss_reduced, dH, dW,
+                                  accumulate_dW: bool = False, dW_bf16=None, stream=None):
+    """flce_forward_backward_scratch(): flce_forward_backward on the library's
+    own scratch array.  Every output is the caller's (nothing is allocated
+    here either); loss_reduced and dW_bf16 may be None.  Returns None."""
+    import torch
+    T, d, V = plan.T, plan.d, plan.V
+    et = _elem_dtype(plan)
+    if reduction not in _REDUCTIONS:
+        raise ValueError(f"unknown reduction {reduction!r}")
+    for name, t in (("loss", loss), ("lse", lse), ("dH", dH), ("dW", dW)):
+        if t is None:
+            raise ValueError(f"{name} must be given: this call allocates nothing")
+    _check_tensor("H", H, (T, d), et)
+    _check_tensor("W", W, (V, d), et)
+    _check_tensor("y", y, (T,), torch.int64)
+    _check_tensor("loss", loss, (T,), torch.float32)
+    _check_tensor("lse", lse, (T,), torch.float32)
+    _check_tensor("loss_reduced", loss_reduced, (1,), torch.float32)
+    _check_tensor("dH", dH, (T, d), et)
+    _check_tensor("dW", dW, (V, d), torch.float32)
+    _check_tensor("dW_bf16", dW_bf16, (V, d), torch.bfloat16)
+    _check(load().flce_forward_backward_scratch(
+        ctypes.byref(plan), _ptr(H), _ptr(W), _ptr(y), int(ignore_index), _REDUCTIONS[reduction],
+        float(scale), _ptr(loss), _ptr(lse), _ptr(loss_reduced), _ptr(dH), _ptr(dW),
+        1 if accumulate_dW else 0, _ptr(dW_bf16), _stream(stream)))

@@ -35,6 +35,9 @@ constexpr int64_t kComputeUnits = 256;  // MI355X
 constexpr uint64_t kScalarBytes = 256;
 
 thread_local char g_err[512] = "";
+// set while an allocation-free call runs: its launches are not timed (timing
+// would create hipEvents)
+thread_local bool g_untimed = false;
 
 flce_status_t fail(flce_status_t st, const char* fmt, ...) {
   va_list ap;
@@ -109,6 +112,7 @@ hipEvent_t pooled_event(Timing& t) {
 class Timed {
  public:
   Timed(hipStream_t s, KernelId kid, double flops, double bytes) : s_(s) {
+    if (g_untimed) return;
     Timing& t = timing();
     std::lock_guard<std::mutex> g(t.mu);
     if (!t.enabled) return;
@@ -688,6 +692,30 @@ flce_status_t flce_forward_backward(const flce_plan_t* plan, const void* H, cons
     if (e != hipSuccess) return hip_fail(e, "dW cast launch");
   }
   return ok();
+}
+
+flce_status_t flce_forward_backward_scratch(const flce_plan_t* plan, const void* H,
+                                            const void* W, const int64_t* y, int64_t ignore_index,
+                                            flce_reduction_t reduction, float scale, float* loss,
+                                            float* lse, float* loss_reduced, void* dH, float* dW,
+                                            int accumulate_dW, void* dW_bf16, void* stream) {
+  flce_status_t st = check_plan(plan);
+  if (st != FLCE_OK) return st;
+  const uint64_t cap = flce::scratch_bytes();
+  if (plan->ws_bytes > cap)
+    return fail(FLCE_ERR_WORKSPACE,
+                "the plan needs %llu workspace bytes; the scratch array holds %llu (plan with "
+                "vocab_ws_cap_bytes <= %llu)",
+                (unsigned long long)plan->ws_bytes, (unsigned long long)cap,
+                (unsigned long long)(cap - kScalarBytes));
+  void* ws = nullptr;
+  const hipError_t e = flce::scratch_address(&ws);
+  if (e != hipSuccess) return hip_fail(e, "scratch array address");
+  g_untimed = true;
+  st = flce_forward_backward(plan, H, W, y, ignore_index, reduction, scale, loss, lse,
+                             loss_reduced, dH, dW, accumulate_dW, dW_bf16, ws, cap, stream);
+  g_untimed = false;
+  return st;
 }
 
 flce_status_t flce_forward_shard(const flce_plan_t* plan, const void* H, const void* W_shard,

@@ -37,6 +37,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "flce_launch.h"
 #include "flce_tile.hpp"
 
@@ -1275,6 +1277,38 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
   return hipGetLastError();
+}
+
+// ============================================================= scratch array
+// The workspace of the allocation-free entry point (for callers that cannot
+// allocate device memory).  Static device memory: every GPU that runs the
+// library holds its own copy until the process ends.  In host code the
+// array's name is only a stand-in for the device symbol, never an address:
+// scratch_address() looks the device address up once per device, with that
+// device current, and every use goes through that address.
+constexpr uint64_t kScratchBytes = 256ull << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+uint64_t scratch_bytes() { return kScratchBytes; }
+
+hipError_t scratch_address(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 TileInfo tile_info(bool bf16) {

@@ -174,5 +174,10 @@ hipError_t launch_zero_rows(void* dH, const int* idx, const int* tv, int64_t T, 
 hipError_t launch_gather_block(const void* H, const TokBlock& blk, int d, void* Hc, void* Ht,
                                bool bf16, hipStream_t s);
 hipError_t launch_shard_merge(const ShardMergeArgs& a, hipStream_t s);
+// The library's static device workspace (allocation-free entry point): its
+// size, and its device address on the current device (looked up once per
+// device, then cached).
+uint64_t scratch_bytes();
+hipError_t scratch_address(void** out);
 
 }  // namespace flce

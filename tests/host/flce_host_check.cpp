@@ -88,6 +88,13 @@ TileInfo tile_info(bool bf16) {
   return t;
 }
 int64_t compact_chunks(int64_t T) { return (T + 4095) / 4096; }
+// the static scratch array: a fake buffer registered per case by the driver
+uintptr_t g_scratch = 0;
+uint64_t scratch_bytes() { return FLCE_SCRATCH_BYTES; }
+hipError_t scratch_address(void** out) {
+  *out = reinterpret_cast<void*>(g_scratch);
+  return hipSuccess;
+}
 int dh_split_slots() { return 256; }
 
 static double esz(bool bf16) { return bf16 ? 2.0 : 4.0; }
@@ -308,6 +315,7 @@ void run_case(int64_t T, int64_t d, int64_t V, int dt, unsigned long long cap) {
   const void* lse2 = buf("lse_shards", 2.0 * T * 4);
   const void* zt2 = buf("zt_shards", 2.0 * T * 4);
   const uint64_t wsb = plan.ws_bytes;
+  flce::g_scratch = reinterpret_cast<uintptr_t>(buf("scratch", (double)FLCE_SCRATCH_BYTES));
   reset();
 
   // ---- every entry point on the plan
@@ -333,6 +341,14 @@ void run_case(int64_t T, int64_t d, int64_t V, int dt, unsigned long long cap) {
                                           p<float>(lse), p<float>(red), p<void>(dH), p<float>(dW),
                                           0, p<void>(b16), p<void>(ws), wsb, nullptr),
                     FLCE_OK, "forward_backward");
+  // the allocation-free variant: the plan fits the scratch array, or the
+  // call is refused before any launch
+  expect_status(flce_forward_backward_scratch(&plan, H, W, p<int64_t>(y), -100,
+                                              FLCE_REDUCE_MEAN_VALID, 1.f, p<float>(loss),
+                                              p<float>(lse), p<float>(red), p<void>(dH),
+                                              p<float>(dW), 1, p<void>(dWb), nullptr),
+                plan.ws_bytes <= FLCE_SCRATCH_BYTES ? FLCE_OK : FLCE_ERR_WORKSPACE,
+                "forward_backward_scratch");
   // this plan as a shard [vs, vs + V) of a vocabulary of vt ids
   const int64_t vt = V + 9 < ((int64_t)1 << 31) ? V + 9 : ((int64_t)1 << 31) - 1;
   const int64_t vs = (vt - V) / 2;

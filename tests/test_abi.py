@@ -63,6 +63,31 @@ def test_plan_struct_layout_matches_header(tmp_path):
     assert out[1:] == [getattr(flce.Plan, f).offset for f in fields]
 
 
+def test_scratch_size_constant_matches_header(tmp_path):
+    """FLCE_SCRATCH_BYTES of the binding is the header's."""
+    src = tmp_path / "scratch.c"
+    src.write_text("#include <stdio.h>\n#include \"flce.h\"\n"
+                   "int main(void) { printf(\"%llu\\n\", FLCE_SCRATCH_BYTES); return 0; }\n")
+    exe = tmp_path / "scratch"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    assert int(out) == flce.FLCE_SCRATCH_BYTES
+
+
+def test_scratch_call_refuses_a_plan_beyond_the_array(lib):
+    """A plan whose workspace exceeds the scratch array is refused before any
+    device call (the default plan at 65,536 x 2,048 x 124,160 needs 902 MB)."""
+    p = flce.flce_plan(65536, 2048, 124160, flce.FLCE_BF16)
+    assert p.ws_bytes > flce.FLCE_SCRATCH_BYTES
+    st = lib.flce_forward_backward_scratch(ctypes.byref(p), 16, 16, 16, -100, 0, 1.0, 16, 16,
+                                           None, 16, 16, 0, None, None)
+    assert st == flce.FLCE_ERR_WORKSPACE
+    assert "scratch" in flce.last_error()
+    q = flce.flce_plan(65536, 2048, 124160, flce.FLCE_BF16, flce.FLCE_SCRATCH_BYTES - 256)
+    assert q.ws_bytes <= flce.FLCE_SCRATCH_BYTES
+
+
 def test_version_and_status_strings(lib):
     assert flce.version() == "0.1.0"
     for st in (0, -1, -2, -3, -4):

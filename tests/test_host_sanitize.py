@@ -39,6 +39,9 @@ CASES = [
     (384, 8192, 131200, BF, 0), (131100, 8192, 1000, BF, 0), (1000, 4096, 1 << 18, F, 0),
     (4096, 65536, 50000, BF, 0), (64, 65536, 300, F, 0), (200_000_000, 8, 3, F, 0),
     (1000, 8, (1 << 31) - 1, BF, 0),
+    # sized for the allocation-free variant's scratch array
+    (6000, 1024, 30000, BF, flce.FLCE_SCRATCH_BYTES - 256),
+    (65536, 2048, 124160, BF, flce.FLCE_SCRATCH_BYTES - 256),
     # rejected by the planner
     (-1, 128, 1000, BF, 0), (10, 0, 1000, BF, 0), (10, 128, 0, BF, 0), (10, 12, 1000, BF, 0),
     (10, 65544, 1000, BF, 0), (1 << 31, 128, 1000, BF, 0), ((1 << 31) - 1, 8, 3, F, 0),
