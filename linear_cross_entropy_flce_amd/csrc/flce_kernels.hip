@@ -117,16 +117,23 @@ struct LogitCfg<float> {
   using T = SmallTile<float, true, true, FLCE_LOGIT_NS>;
 };
 
-// dH (A = dZ K-contiguous, B = W MN-contiguous).
+// dH, computed as its transpose dH^T = W[slab]^T dZ^T: M = hidden, N = tokens,
+// K = slab vocab (A = W MN-contiguous, B = dZ K-contiguous), so that each
+// lane's accumulator quads are four consecutive hidden units of one token row
+// (16-byte accumulator and dH accesses, one token lookup per column).  The
+// bf16 tile's 8 waves are 4 x 2 (64 hidden x 128 tokens each): measured as
+// fast as the untransposed 2 x 4 product, where 2 x 4 with A MN-contiguous
+// was 2% slower.
 template <typename E>
 struct DhCfg;
 template <>
 struct DhCfg<__bf16> {
-  using T = BigTile<__bf16, true, false, FLCE_DH_NS, FLCE_DH_KB, FLCE_DH_DMA>;
+  using T = Tile<256, 256, 4, 2, __bf16, false, true, FLCE_DH_KB, FLCE_DH_NS,
+                 FLCE_DH_DMA || FLCE_DH_NS != 2>;
 };
 template <>
 struct DhCfg<float> {
-  using T = SmallTile<float, true, false, FLCE_DH_NS>;
+  using T = SmallTile<float, false, true, FLCE_DH_NS>;
 };
 template <typename E>
 struct DwCfg;
@@ -633,15 +640,37 @@ __device__ __forceinline__ int dh_splits(const DhArgs& a, int act_m) {
   return max(1, min(kDhSplitSlots / tiles, stages));
 }
 
-// Part `sp` of S of the tile (tm, tn), as stored by the dH kernel: register r
-// of block (i, j) of thread x at ((i * NI + j) * 16 + r) * NT + x, so that
-// every store and load of a register is NT consecutive floats.
+// Part `sp` of S of the tile (tm, tn), as stored by the dH kernel: row-major
+// [token column][hidden row] fp32, i.e. dH's own orientation, so that the
+// reduce pass reads every part and writes the accumulator / dH rows
+// contiguously; the dH kernel's stores are 16-byte quads of four hidden units.
 template <typename TL>
 __device__ __forceinline__ float* dh_part(const DhArgs& a, int act_m, int sp, int tm, int tn) {
   return a.part + ((int64_t)(sp * act_m + tm) * a.n_ntiles + tn) * (TL::BM * TL::BN);
 }
 
-// The mode epilogue of one finished tile (rows tl0.., hidden columns n0..).
+// Applies the mode to four consecutive hidden units of token row tl of the
+// block: v (+)= accumulator, then the accumulator or the token's dH row.
+template <typename E>
+__device__ __forceinline__ void dh_quad(const DhArgs& a, f32x4_t v, int64_t tl, int64_t n,
+                                        int64_t t_row) {
+  f32x4_t* accp = reinterpret_cast<f32x4_t*>(a.dh_acc + tl * a.d + n);
+  if (a.mode == 1 || a.mode == 2) v += *accp;
+  if (a.mode == 0 || a.mode == 1) {
+    *accp = v;
+  } else {
+    E* out = reinterpret_cast<E*>(a.dH) + t_row * a.d + n;
+    if constexpr (sizeof(E) == 2) {
+      *reinterpret_cast<bf16x4_t*>(out) = bf16x4_t{(E)v[0], (E)v[1], (E)v[2], (E)v[3]};
+    } else {
+      *reinterpret_cast<f32x4_t*>(out) = v;
+    }
+  }
+}
+
+// The mode epilogue of one finished tile (hidden rows n0.. of the transposed
+// tile, token columns tl0..): per token column one lookup of the token's own
+// row, then 16-byte accesses of four consecutive hidden units.
 template <typename E, typename TL>
 __device__ __forceinline__ void dh_store(const DhArgs& a, const TL& tile, int64_t tl0, int64_t n0,
                                          int t_count) {
@@ -649,24 +678,19 @@ __device__ __forceinline__ void dh_store(const DhArgs& a, const TL& tile, int64_
   const int wm = wave / TL::WN, wn = wave % TL::WN;
 #pragma unroll
   for (int j = 0; j < TL::NI; ++j) {
-    const int64_t n = n0 + TL::col_of(wn, j);
-    if (n >= a.d) continue;
+    const int64_t tl = tl0 + TL::col_of(wn, j);  // token within the block
+    if (tl >= t_count) continue;
+    const int64_t t_row = a.mode >= 2 ? (int64_t)a.blk.idx[a.blk.t_begin + tl] : 0;
 #pragma unroll
     for (int i = 0; i < TL::MI; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t tl = tl0 + TL::row_of(wm, i, r);
-        if (tl >= t_count) continue;
-        float v = tile.acc[i][j][r];
-        float* accp = a.dh_acc + tl * a.d + n;
-        if (a.mode == 1 || a.mode == 2) v += *accp;
-        if (a.mode == 0 || a.mode == 1) {
-          *accp = v;
-        } else {
-          const int64_t t = a.blk.idx[a.blk.t_begin + tl];  // the token's own row
-          E* out = reinterpret_cast<E*>(a.dH) + t * a.d + n;
-          *out = (E)v;
-        }
+      for (int q = 0; q < 4; ++q) {
+        // d is a multiple of 8 and n of 4: the four units are all in range or none
+        const int64_t n = n0 + TL::row_of(wm, i, 4 * q);
+        if (n >= a.d) continue;
+        dh_quad<E>(a, f32x4_t{tile.acc[i][j][4 * q], tile.acc[i][j][4 * q + 1],
+                              tile.acc[i][j][4 * q + 2], tile.acc[i][j][4 * q + 3]},
+                   tl, n, t_row);
       }
   }
 }
@@ -677,35 +701,35 @@ __device__ __forceinline__ void dh_body(const DhArgs& a, int bid, char* lds) {
   using TL = typename DhCfg<E>::T;
   constexpr int ESZ = TL::ESZ;
   const int t_count = block_count(a.blk);
-  const int act_m = (t_count + TL::BM - 1) / TL::BM;
+  const int act_m = (t_count + TL::BN - 1) / TL::BN;  // token tiles
   const int S = dh_splits<TL>(a, act_m);
   // split-major virtual token tiles: the workgroups an XCD runs together
   // share one part's W panels
   int tv, tn;
   if (!xcd_tile(bid, act_m * S, a.n_ntiles, 4, tv, tn)) return;
   const int sp = tv / act_m, tm = tv % act_m;
-  const int64_t tl0 = (int64_t)tm * TL::BM;  // token within block
-  const int64_t n0 = (int64_t)tn * TL::BN;   // hidden index
+  const int64_t tl0 = (int64_t)tm * TL::BN;  // token within block
+  const int64_t n0 = (int64_t)tn * TL::BM;   // hidden index
   const int stages = (a.k_count + TL::BK - 1) / TL::BK;
   const int k_lo = (int)((int64_t)stages * sp / S) * TL::BK;
   const int k_hi = min(a.k_count, (int)((int64_t)stages * (sp + 1) / S) * TL::BK);
   const int K = k_hi - k_lo;  // >= 1: S <= stages
 
   Operand A, B;
-  A.rs = make_rsrc(a.dz, clamp_bytes((int64_t)t_count * a.ldz * ESZ));
-  A.off = (uint32_t)((tl0 * a.ldz + k_lo) * ESZ);
-  A.ld_bytes = (uint32_t)(a.ldz * ESZ);
-  A.rows = (int)min<int64_t>(TL::BM, t_count - tl0);
-  A.cols = K;
   // W rows of this part of the slab, based at the part's first row: the
   // planner keeps a slab's rows (K x d elements) below 2^31 bytes, so W
   // itself may be larger
-  B.rs = make_rsrc(reinterpret_cast<const char*>(a.W) + (a.v_begin + k_lo) * a.d * ESZ,
+  A.rs = make_rsrc(reinterpret_cast<const char*>(a.W) + (a.v_begin + k_lo) * a.d * ESZ,
                    clamp_bytes((int64_t)K * a.d * ESZ));
-  B.off = (uint32_t)(n0 * ESZ);
-  B.ld_bytes = (uint32_t)(a.d * ESZ);
-  B.rows = K;
-  B.cols = (int)min<int64_t>(TL::BN, a.d - n0);
+  A.off = (uint32_t)(n0 * ESZ);
+  A.ld_bytes = (uint32_t)(a.d * ESZ);
+  A.rows = K;
+  A.cols = (int)min<int64_t>(TL::BM, a.d - n0);
+  B.rs = make_rsrc(a.dz, clamp_bytes((int64_t)t_count * a.ldz * ESZ));
+  B.off = (uint32_t)((tl0 * a.ldz + k_lo) * ESZ);
+  B.ld_bytes = (uint32_t)(a.ldz * ESZ);
+  B.rows = (int)min<int64_t>(TL::BN, t_count - tl0);
+  B.cols = K;
 
   TL tile;
   tile.zero();
@@ -717,61 +741,50 @@ __device__ __forceinline__ void dh_body(const DhArgs& a, int bid, char* lds) {
     return;
   }
   float* pt = dh_part<TL>(a, act_m, sp, tm, tn);
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / TL::WN, wn = wave % TL::WN;
 #pragma unroll
-  for (int i = 0; i < TL::MI; ++i)
+  for (int j = 0; j < TL::NI; ++j) {
+    float* row = pt + TL::col_of(wn, j) * TL::BM;
 #pragma unroll
-    for (int j = 0; j < TL::NI; ++j)
+    for (int i = 0; i < TL::MI; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        pt[((i * TL::NI + j) * 16 + r) * TL::NT + threadIdx.x] = tile.acc[i][j][r];
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4_t*>(row + TL::row_of(wm, i, 4 * q)) =
+            f32x4_t{tile.acc[i][j][4 * q], tile.acc[i][j][4 * q + 1], tile.acc[i][j][4 * q + 2],
+                    tile.acc[i][j][4 * q + 3]};
+  }
 }
 
 // Sum of a split dH's parts in ascending part order, then the mode epilogue,
-// as an elementwise pass: each thread takes four consecutive floats of a
-// partial tile's register-major layout, which are four consecutive hidden
-// columns of one token row (lanes 4c..4c+3 of one register), so partials are
-// read as 16-byte vectors and the accumulator / dH rows are accessed four
-// columns at a time.  Nothing to do when the dH kernel ran unsplit (S = 1).
+// as an elementwise pass over 16-byte quads (four consecutive hidden units of
+// one token row): consecutive threads take consecutive quads of a token row,
+// so the parts and the accumulator / dH rows are all accessed contiguously.
+// Nothing to do when the dH kernel ran unsplit (S = 1).
 template <typename E>
 __global__ void __launch_bounds__(256) bwd_dh_reduce_kernel(DhArgs a) {
-  using TL = typename DhCfg<E>::T;
+  using TL = typename DhCfg<E>::T;  // transposed tile: M = hidden, N = tokens
   const int t_count = block_count(a.blk);
-  const int act_m = (t_count + TL::BM - 1) / TL::BM;
+  const int act_m = (t_count + TL::BN - 1) / TL::BN;
   const int S = dh_splits<TL>(a, act_m);
   if (S == 1) return;
-  constexpr int kQuads = TL::BM * TL::BN / 4;  // 4-float groups per tile
+  constexpr int kQuads = TL::BM * TL::BN / 4;  // quads per tile
   const int64_t n_units = (int64_t)act_m * a.n_ntiles * kQuads;
   for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < n_units;
        u += (int64_t)gridDim.x * 256) {
     const int tile = (int)(u / kQuads);
-    const int e = (int)(u % kQuads) * 4;  // element in the register-major tile
+    const int e = (int)(u % kQuads) * 4;           // element of the row-major part
+    const int c = e / TL::BM, m = e % TL::BM;      // token column, hidden row
     const int tm = tile / a.n_ntiles, tn = tile % a.n_ntiles;
+    const int64_t tl = (int64_t)tm * TL::BN + c;
+    const int64_t n = (int64_t)tn * TL::BM + m;
+    // d is a multiple of 8 and n of 4: the four units are all in range or none
+    if (tl >= t_count || n >= a.d) continue;
     f32x4_t v = {0.f, 0.f, 0.f, 0.f};
     for (int sp = 0; sp < S; ++sp)
       v += *reinterpret_cast<const f32x4_t*>(dh_part<TL>(a, act_m, sp, tm, tn) + e);
-    // element e = (register reg, thread x): reg = (i * NI + j) * 16 + r
-    const int reg = e / TL::NT, x = e % TL::NT;
-    const int r = reg % 16, ij = reg / 16, i = ij / TL::NI, j = ij % TL::NI;
-    const int wave = x / 64, lane = x % 64;
-    const int wm = wave / TL::WN, wn = wave % TL::WN;
-    const int64_t tl = (int64_t)tm * TL::BM + wm * TL::WTM + i * 32 + 8 * (r >> 2) +
-                       4 * (lane >> 5) + (r & 3);
-    const int64_t n = (int64_t)tn * TL::BN + wn * TL::WTN + j * 32 + (lane & 31);
-    // d is a multiple of 8 and n of 4: the four columns are all in range or none
-    if (tl >= t_count || n >= a.d) continue;
-    f32x4_t* accp = reinterpret_cast<f32x4_t*>(a.dh_acc + tl * a.d + n);
-    if (a.mode == 1 || a.mode == 2) v += *accp;
-    if (a.mode == 0 || a.mode == 1) {
-      *accp = v;
-    } else {
-      const int64_t t = a.blk.idx[a.blk.t_begin + tl];
-      E* out = reinterpret_cast<E*>(a.dH) + t * a.d + n;
-      if constexpr (sizeof(E) == 2) {
-        *reinterpret_cast<bf16x4_t*>(out) = bf16x4_t{(E)v[0], (E)v[1], (E)v[2], (E)v[3]};
-      } else {
-        *reinterpret_cast<f32x4_t*>(out) = v;
-      }
-    }
+    const int64_t t_row = a.mode >= 2 ? (int64_t)a.blk.idx[a.blk.t_begin + tl] : 0;
+    dh_quad<E>(a, v, tl, n, t_row);
   }
 }
 
@@ -1316,16 +1329,16 @@ TileInfo tile_info(bool bf16) {
   if (bf16) {
     t.logit_bm = LogitCfg<__bf16>::T::BM;
     t.logit_bn = LogitCfg<__bf16>::T::BN;
-    t.dh_bm = DhCfg<__bf16>::T::BM;
-    t.dh_bn = DhCfg<__bf16>::T::BN;
+    t.dh_bm = DhCfg<__bf16>::T::BN;  // tokens (the transposed tile's N)
+    t.dh_bn = DhCfg<__bf16>::T::BM;  // hidden
     t.dw_bm = DwCfg<__bf16>::T::BM;
     t.dw_bn = DwCfg<__bf16>::T::BN;
     t.dh_bk = DhCfg<__bf16>::T::BK;
   } else {
     t.logit_bm = LogitCfg<float>::T::BM;
     t.logit_bn = LogitCfg<float>::T::BN;
-    t.dh_bm = DhCfg<float>::T::BM;
-    t.dh_bn = DhCfg<float>::T::BN;
+    t.dh_bm = DhCfg<float>::T::BN;
+    t.dh_bn = DhCfg<float>::T::BM;
     t.dw_bm = DwCfg<float>::T::BM;
     t.dw_bn = DwCfg<float>::T::BN;
     t.dh_bk = DhCfg<float>::T::BK;
