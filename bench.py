@@ -69,12 +69,7 @@ def cpu_baseline(inp, cfg, n_rows: int):
 
     import oracle
     import workloads as wl
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
-    except Exception:  # threadpoolctl missing: report the core count
-        threads = os.cpu_count() or 1
+    threads = blas_threads()
     if cfg in wl.CONFIGS:
         rows = wl.sample_rows(cfg, n_rows)
     else:
@@ -119,9 +114,10 @@ def measured_traffic(kernel: str, workload: str, plan_key: dict):
     return None
 
 
-def elf_section(path: str, name: str):
-    """Bytes of the named section of a 64-bit little-endian ELF file, or None."""
-    data = open(path, "rb").read()
+def elf_section(path, name: str):
+    """Bytes of the named section of a 64-bit little-endian ELF file (a path,
+    or the file's bytes), or None."""
+    data = path if isinstance(path, (bytes, bytearray)) else open(path, "rb").read()
     if data[:4] != b"\x7fELF" or data[4] != 2 or data[5] != 1:
         return None
     shoff, = struct.unpack_from("<Q", data, 0x28)
@@ -139,16 +135,37 @@ def elf_section(path: str, name: str):
     return None
 
 
+def gfx950_text(fatbin: bytes):
+    """The .text section (the kernels' machine code) of the gfx950 code object
+    inside a clang offload bundle, or None."""
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    if fatbin[:len(magic)] != magic:
+        return None
+    n, = struct.unpack_from("<Q", fatbin, len(magic))
+    p = len(magic) + 8
+    for _ in range(n):
+        off, size, tlen = struct.unpack_from("<QQQ", fatbin, p)
+        p += 24
+        triple = fatbin[p:p + tlen].decode(errors="replace")
+        p += tlen
+        if triple.endswith("gfx950"):
+            return elf_section(fatbin[off:off + size], ".text")
+    return None
+
+
 def device_code_digest(lib_path: str = None):
-    """SHA-256 of the GPU code objects embedded in libflce.so (its
-    .hip_fatbin section): unchanged by host-only or comment edits, changed
-    by any edit that changes a kernel."""
+    """SHA-256 of the gfx950 machine code in libflce.so: the .text section of
+    the code object in its .hip_fatbin bundle.  Unchanged by host-only or
+    comment edits and by where the library is built (the bundle's other
+    sections carry a per-build id), changed by any edit that changes a
+    kernel."""
     import hashlib
     if lib_path is None:
         from linear_cross_entropy_flce_amd import _lib
         lib_path = _lib.LIB_PATH
     try:
-        code = elf_section(lib_path, ".hip_fatbin")
+        fatbin = elf_section(lib_path, ".hip_fatbin")
+        code = gfx950_text(fatbin) if fatbin is not None else None
     except (OSError, ValueError, IndexError, struct.error):
         return None
     return None if code is None else hashlib.sha256(code).hexdigest()
@@ -223,7 +240,7 @@ def summarize_traffic(fetch_csv: str, write_csv: str, cfetch_csv: str, cwrite_cs
         "about": "HBM traffic per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per "
                  "dispatch), each divided by the value the same counter reads per byte of a plain "
                  "1 GiB device copy (bench.py --copy-calibration 1024). Valid only while "
-                 "libflce.so's GPU code (.hip_fatbin) hashes to device_code_sha256 and the "
+                 "libflce.so's gfx950 machine code (.text of its code object) hashes to device_code_sha256 and the "
                  "workload's plan is the one recorded.",
         "workload": workload,
         "device_code_sha256": device_code_digest(),
@@ -411,6 +428,165 @@ def forms_leg(flce, wl, plan, H, W, y, ws, stream, reps: int):
     return outs
 
 
+def config_leg(flce, wl, cfg, steps: int, warmup: int, oracle_rows):
+    """One workload configuration, measured like the headline step: forward +
+    backward with inputs resident, hipEvents on the stream around each
+    forward and backward, the device memory the step holds, and the oracle's
+    host time (all rows when `oracle_rows` is None, else that many seeded rows
+    with the full-batch time extrapolated from them)."""
+    import numpy as np
+    import torch
+    log(f"config {cfg.index} {cfg.name}: inputs")
+    torch.cuda.empty_cache()
+    free_before = torch.cuda.mem_get_info()[0]
+    inp = wl.config_inputs(cfg)
+    dev = torch.device("cuda:0")
+    bf16 = cfg.dtype == wl.DTYPE_BF16
+    if bf16:
+        H = torch.from_numpy(inp.H.view(np.int16)).to(dev).view(torch.bfloat16)
+        W = torch.from_numpy(inp.W.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        H = torch.from_numpy(inp.H).to(dev)
+        W = torch.from_numpy(inp.W).to(dev)
+    y = torch.from_numpy(inp.y).to(dev)
+    T, d, V = cfg.T, cfg.d, cfg.V
+    ls, gs = cfg.scales()
+    plan = flce.flce_plan(T, d, V, cfg.dtype)
+    torch.cuda.reset_peak_memory_stats()
+    ws = flce.workspace(plan, dev)
+    loss = torch.empty(T, dtype=torch.float32, device=dev)
+    lse = torch.empty(T, dtype=torch.float32, device=dev)
+    red = torch.empty(1, dtype=torch.float32, device=dev)
+    dH = torch.empty((T, d), dtype=H.dtype, device=dev)
+    dW = torch.empty((V, d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+
+    def step(e=None):
+        if e: e[0].record(stream)
+        flce.flce_forward(plan, H, W, y, wl.IGNORE_INDEX, ls, loss=loss, lse=lse, loss_reduced=red,
+                          ws=ws, stream=stream)
+        if e: e[1].record(stream)
+        flce.flce_backward(plan, H, W, y, lse, wl.IGNORE_INDEX, gs, dH=dH, dW=dW, ws=ws,
+                           stream=stream)
+        if e: e[2].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    fwd = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    bwd = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    ms = sum(e[0].elapsed_time(e[2]) for e in ev) / steps
+    peak_alloc = torch.cuda.max_memory_allocated()
+    used = free_before - torch.cuda.mem_get_info()[0]
+    t_valid = int((inp.y != wl.IGNORE_INDEX).sum())
+    counted = 8.0 * T * d * V
+    effective = 2.0 * T * d * V + 6.0 * t_valid * d * V
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
+    out = {"workload": cfg.name, "T": T, "d": d, "V": V, "dtype": cfg.dtype,
+           "reduction": cfg.reduction, "valid_tokens": t_valid, "steps": steps,
+           "ms_per_step": round(ms, 4), "fwd_ms_median": round(fwd[len(fwd) // 2], 4),
+           "bwd_ms_median": round(bwd[len(bwd) // 2], 4),
+           "counted_tflops": round(counted / ms / 1e9, 2),
+           "effective_tflops": round(effective / ms / 1e9, 2),
+           "mfma_peak": peak, "mfma_peak_frac": round(counted / ms / 1e9 / peak, 4),
+           "peak_allocated_bytes": int(peak_alloc), "device_used_delta_bytes": int(used),
+           "workspace_bytes": int(plan.ws_bytes),
+           "vocab_axis_workspace_bytes": int(plan.dz_ws_bytes),
+           "naive_logits_one_copy_bytes": int(plan.naive_logits_bytes),
+           "plan": {"fwd_splits": plan.fwd_splits, "bwd_block": plan.bwd_block,
+                    "bwd_slab": plan.bwd_slab, "n_blocks": plan.n_blocks, "n_slabs": plan.n_slabs}}
+    log(f"  {ms:.3f} ms/step (fwd {out['fwd_ms_median']:.3f}, bwd {out['bwd_ms_median']:.3f}), "
+        f"{out['counted_tflops']:.1f} counted / {out['effective_tflops']:.1f} effective TFLOP/s, "
+        f"peak allocated {peak_alloc / 1e9:.2f} GB, vocab-axis workspace "
+        f"{plan.dz_ws_bytes / 1e9:.3f} GB")
+    del H, W, y, ws, loss, lse, red, dH, dW
+    torch.cuda.empty_cache()
+    if oracle_rows != 0:
+        out["oracle"] = oracle_time(wl, cfg, inp, oracle_rows)
+    return out
+
+
+def oracle_time(wl, cfg, inp, rows):
+    """The oracle (numpy float64) on this host: the whole batch when `rows` is
+    None, else `rows` seeded token rows (their loss, lse, dH and dW terms, i.e.
+    the whole step for those rows) with the full-batch time extrapolated."""
+    import oracle
+    threads = blas_threads()
+    ls, gs = cfg.scales()
+    Wf = inp.W_f32()
+    if rows is None:
+        t0 = time.perf_counter()
+        oracle.forward_backward(inp.H_f32(), Wf, inp.y, wl.IGNORE_INDEX, gs, row_chunk=256)
+        dt = time.perf_counter() - t0
+        log(f"  oracle: full batch in {dt:.1f} s on {threads} threads")
+        return {"kind": "oracle", "seconds": round(dt, 2), "rows": cfg.T, "full": True,
+                "cores": threads}
+    r = wl.sample_rows(cfg, rows)
+    Hs = inp.H_f32()[r]
+    t0 = time.perf_counter()
+    oracle.forward_backward(Hs, Wf, inp.y[r], wl.IGNORE_INDEX, gs, row_chunk=256)
+    dt = time.perf_counter() - t0
+    ext = dt * cfg.T / len(r)
+    log(f"  oracle: {len(r)} rows in {dt:.1f} s on {threads} threads "
+        f"(whole batch extrapolated: {ext:.0f} s)")
+    return {"kind": "oracle", "seconds": round(dt, 2), "rows": int(len(r)), "full": False,
+            "cores": threads, "extrapolated_full_batch_s": round(ext, 1),
+            "note": "the sampled rows' step (loss, lse, dH, dW terms) timed; the whole-batch "
+                    "figure is that rate over T rows, an extrapolation"}
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()
+                    if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: report the core count
+        return os.cpu_count() or 1
+
+
+def library_gemm_leg(reps: int = 10):
+    """The three GEMM shapes of one token block and vocab slab at the pages'
+    shape, as plain library products (torch.matmul, which runs hipBLASLt), on
+    data of the workload's distributions: the logits (8,192 x 2,048 times
+    2,048 x 46,848), dH (8,192 x 46,848 times 46,848 x 2,048) and dW
+    (46,848 x 8,192 times 8,192 x 2,048).  Every operand is a contiguous
+    row-major bf16 matrix; hipEvents around `reps` products each."""
+    import torch
+    dev = torch.device("cuda:0")
+    g = torch.Generator(dev).manual_seed(11)
+    B, d, Vs = 8192, 2048, 46848
+    Hb = torch.randn((B, d), device=dev, generator=g).to(torch.bfloat16)
+    Wt = (0.02 * torch.randn((d, Vs), device=dev, generator=g)).to(torch.bfloat16)
+    Ws = Wt.t().contiguous()
+    # a dZ block with the magnitudes of softmax - onehot at this shape
+    dZ = (torch.rand((B, Vs), device=dev, generator=g) * (2.0 / Vs)).to(torch.bfloat16)
+    dZt = dZ.t().contiguous()
+    shapes = {"logits": (Hb, Wt), "dH": (dZ, Ws), "dW": (dZt, Hb)}
+    out = {}
+    for name, (a, b) in shapes.items():
+        c = torch.matmul(a, b)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(a, b, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        fl = 2.0 * a.shape[0] * a.shape[1] * b.shape[1]
+        out[name] = {"M": a.shape[0], "K": a.shape[1], "N": b.shape[1], "ms": round(ms, 4),
+                     "tflops": round(fl / ms / 1e9, 1)}
+        log(f"  library GEMM {name}: {a.shape[0]} x {a.shape[1]} x {b.shape[1]}: {ms:.3f} ms, "
+            f"{fl / ms / 1e9:.1f} TFLOP/s")
+        del c
+    return out
+
+
 def copy_calibration(mib: int):
     """A plain copy of mib MiB (read mib, write mib), three times: the byte
     counters of a profiler run over it give the scale of FETCH_SIZE and
@@ -443,6 +619,16 @@ def main():
                          "vocabulary; fused call; token scoring); 0 skips them")
     ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="rows of the CPU-oracle sample (0 skips it)")
+    ap.add_argument("--configs", default="0,1,2,4",
+                    help="other workload configurations timed after the headline one (comma "
+                         "list of indices, or 'none')")
+    ap.add_argument("--data", choices=("random", "zeros", "const"), default="random",
+                    help="headline inputs: the workload's seeded draws (default), or H and W "
+                         "all zero, or constant (1 and 1/64): the same launches on data that "
+                         "toggles no multiplier bits, to measure how much of the step time "
+                         "is data-dependent power")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="also time the block/slab GEMM shapes as plain torch.matmul (hipBLASLt)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this many MiB (a known-size "
                          "reference for the HBM byte counters) and exit")
@@ -503,6 +689,12 @@ def main():
         H = torch.from_numpy(inp.H).to(dev)
         W = torch.from_numpy(inp.W).to(dev)
     y = torch.from_numpy(inp.y).to(dev)
+    if args.data == "zeros":
+        H.zero_()
+        W.zero_()
+    elif args.data == "const":
+        H.fill_(1.0)
+        W.fill_(1.0 / 64)
     T, d, V = cfg.T, cfg.d, cfg.V
     ls, gs = cfg.scales()
     plan = flce.flce_plan(T, d, V, cfg.dtype)
@@ -576,6 +768,7 @@ def main():
     fused = fused_leg(flce, wl, plan, H, W, y, ws, stream, args.shard_steps) if args.shard_steps > 0 else None
     forms = forms_leg(flce, wl, plan, H, W, y, ws, stream, 2 * args.shard_steps + 1) if args.shard_steps > 0 else None
 
+    lib_gemm = library_gemm_leg() if args.library_gemm else None
     cpu = None
     if args.cpu_rows > 0:
         log(f"cpu baseline: oracle on {args.cpu_rows} rows")
@@ -594,7 +787,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if bf16 else "f32",
-        "data": "synthetic",
+        "data": "synthetic" if args.data == "random" else f"synthetic, H and W {args.data}",
         "config": {"workload": cfg.name, "T": T, "d": d, "V": V, "precision": cfg.dtype,
                    "targets": cfg.targets, "ignored_tokens": cfg.n_ignored,
                    "grad_scale": gs, "parallelism": "single GPU"},
@@ -620,9 +813,22 @@ def main():
         "token_scoring": scoring,
         "fused_call": fused,
         "target_logit_forms": forms,
+        "library_gemm": lib_gemm,
         "plan": {"fwd_splits": plan.fwd_splits, "bwd_block": plan.bwd_block,
                  "bwd_slab": plan.bwd_slab, "n_blocks": plan.n_blocks, "n_slabs": plan.n_slabs},
     }
+    # the other workload configurations, each with its oracle host time (all
+    # rows for the two small ones, a seeded sample with an extrapolation for
+    # the others); the headline's buffers are released first
+    others = [] if args.configs == "none" else [int(c) for c in args.configs.split(",") if c]
+    if others and not args.shape:
+        del H, W, y, ws, loss, lse, dH, dW
+        torch.cuda.empty_cache()
+        oracle_rows = {0: None, 1: None, 2: 1024, 3: 256, 4: 256}
+        out["configs"] = {
+            str(c): config_leg(flce, wl, wl.CONFIGS[c], min(args.steps, 10), min(args.warmup, 2),
+                               oracle_rows[c] if args.cpu_rows > 0 else 0)
+            for c in others if c != cfg.index}
     print(json.dumps(out), flush=True)
 
 

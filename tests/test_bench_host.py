@@ -39,14 +39,21 @@ def _section_span(bench, path, name):
 
 
 def test_device_code_digest_covers_gpu_code_only(bench, libpath, tmp_path):
+    """The digest is the SHA-256 of the gfx950 code object's .text: a changed
+    byte of that machine code changes it; a changed byte of host code, or of
+    the bundle outside the machine code (where the per-build id lives), does
+    not; the same sources built to another path give the same digest."""
     import hashlib
-    code = bench.elf_section(libpath, ".hip_fatbin")
+    fatbin = bench.elf_section(libpath, ".hip_fatbin")
+    code = bench.gfx950_text(fatbin)
     assert code is not None and len(code) > 1024
     assert bench.device_code_digest(libpath) == hashlib.sha256(code).hexdigest()
-    data, start, size = _section_span(bench, libpath, ".hip_fatbin")
-    # a byte of GPU code changed: another digest
+    data = open(libpath, "rb").read()
+    c0 = data.find(code)
+    assert c0 > 0
+    # a byte of gfx950 machine code changed: another digest
     gpu = bytearray(data)
-    gpu[start + size // 2] ^= 0xFF
+    gpu[c0 + len(code) // 2] ^= 0xFF
     (tmp_path / "gpu.so").write_bytes(bytes(gpu))
     assert bench.device_code_digest(str(tmp_path / "gpu.so")) != bench.device_code_digest(libpath)
     # a byte of host code changed: the same digest
@@ -56,7 +63,18 @@ def test_device_code_digest_covers_gpu_code_only(bench, libpath, tmp_path):
     host[t0 + len(text) // 2] ^= 0xFF
     (tmp_path / "host.so").write_bytes(bytes(host))
     assert bench.device_code_digest(str(tmp_path / "host.so")) == bench.device_code_digest(libpath)
+    # a byte of the bundle outside the machine code changed: the same digest
+    f0 = data.find(fatbin)
+    other = bytearray(data)
+    other[f0 + len(fatbin) - 8] ^= 0xFF
+    (tmp_path / "bundle.so").write_bytes(bytes(other))
+    assert bench.device_code_digest(str(tmp_path / "bundle.so")) == bench.device_code_digest(libpath)
     assert bench.elf_section(str(tmp_path / "host.so"), ".no_such_section") is None
+    # the same sources built to another path
+    from linear_cross_entropy_flce_amd import build
+    os.makedirs(tmp_path / "elsewhere")
+    other_lib = build.build(out=str(tmp_path / "elsewhere" / "libflce.so"))
+    assert bench.device_code_digest(other_lib) == bench.device_code_digest(libpath)
 
 
 def test_recorded_traffic_needs_same_code_and_plan(bench, libpath, tmp_path, monkeypatch):
