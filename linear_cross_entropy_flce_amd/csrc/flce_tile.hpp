@@ -65,9 +65,10 @@ __device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t rsrc, ui
 }
 
 // A runtime description of one operand of one workgroup tile.  `rs` covers the
-// whole matrix (every matrix the library reads is below 2 GiB, so 32-bit byte
-// offsets reach all of it and kOOB stays beyond every resource), and `off` is
-// the byte offset of the tile origin inside it.
+// rows the tile reads (based at the tile's first row, or at the first row of
+// the vocab slab part it contracts over), always below 2 GiB, so 32-bit byte
+// offsets reach all of it and kOOB stays beyond every resource; `off` is the
+// byte offset of the tile origin inside it.
 struct Operand {
   __amdgpu_buffer_rsrc_t rs;
   uint32_t off;       // KC: row 0 of the tile, k = 0.  MC: k = 0, first tile column.
