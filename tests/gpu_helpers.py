@@ -146,13 +146,14 @@ def compare(got, ref, dtype, what=("loss", "lse", "dH", "dW"), rows=None, loss_t
 
 
 def run_gpu_shards(inp: wl.Inputs, bounds, loss_scale=1.0, grad_scale=1.0, merge=None,
-                   backward=True, dev=None):
+                   backward=True, dev=None, gather=False):
     """The vocab-parallel path on one GPU: W's rows cut at `bounds` (ascending
     vocab ids, 0 .. V), each shard through flce_forward_shard, the statistics
     stacked as an all-gather would, merged by flce_merge_shards (over the
     shard indices in `merge`, default all in order), then flce_backward_shard
     per shard with the merged lse.  dH is the sum of the shards' partials
-    (what the caller's all-reduce does), dW the concatenation of the slices."""
+    (what the caller's all-reduce does), dW the concatenation of the slices.
+    With `gather`, each shard's forward takes its target logits by index."""
     H, W, y = dev if dev is not None else device_inputs(inp)
     V = inp.V
     shards = list(zip(bounds[:-1], bounds[1:]))
@@ -160,6 +161,8 @@ def run_gpu_shards(inp: wl.Inputs, bounds, loss_scale=1.0, grad_scale=1.0, merge
     plans, stats = [], []
     for (a, b) in shards:
         plan = flce.flce_plan(inp.T, inp.d, b - a, inp.dtype)
+        if gather:
+            plan = gather_plan(plan)
         ws = flce.workspace(plan, W.device)
         lse_s, zt_s = flce.flce_forward_shard(plan, H, W[a:b], y, a, V, inp.ignore_index, ws=ws)
         plans.append((plan, ws))

@@ -10,7 +10,7 @@ import torch
 import linear_cross_entropy_flce_amd as flce
 import oracle
 import workloads as wl
-from gpu_helpers import TOL, compare, device_inputs, log, logit_tol, max_abs
+from gpu_helpers import gather_plan, TOL, compare, device_inputs, log, logit_tol, max_abs
 
 pytestmark = pytest.mark.gpu
 IGN = wl.IGNORE_INDEX
@@ -43,13 +43,18 @@ def _fused(plan, H, W, y, reduction, scale, **kw):
     return {k: (_np(v) if v is not None else None) for k, v in out.items()}
 
 
+@pytest.mark.parametrize("form", ["in_tile", "gather"])
 @pytest.mark.parametrize("dtype", [wl.DTYPE_F32, wl.DTYPE_BF16])
 @pytest.mark.parametrize("T,d,V,ign", [(257, 72, 32007, 0.1), (300, 136, 515, 0.3),
                                        (1100, 64, 2049, 0.0)])
-def test_fused_equals_separate_and_oracle(T, d, V, ign, dtype):
+def test_fused_equals_separate_and_oracle(T, d, V, ign, dtype, form):
+    """The fused call equals the separate calls bit for bit, with either form
+    of the forward's target logit, and both match the oracle."""
     inp = wl.make_inputs(T, d, V, dtype, seed=900 + T, sigma_w=0.5, ignore_frac=ign)
     H, W, y = device_inputs(inp)
     plan = flce.flce_plan(T, d, V, dtype)
+    if form == "gather":
+        plan = gather_plan(plan)
     n_valid = int((inp.y != IGN).sum())
     # sum: g = scale
     a = _fused(plan, H, W, y, "sum", 0.25)

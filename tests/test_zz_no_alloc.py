@@ -13,7 +13,7 @@ import torch
 
 import linear_cross_entropy_flce_amd as flce
 import workloads as wl
-from gpu_helpers import device_inputs, log
+from gpu_helpers import device_inputs, gather_plan, log
 
 pytestmark = pytest.mark.gpu
 
@@ -38,11 +38,13 @@ def _outputs(plan, dev, et, base_dW):
                 dW_bf16=torch.full((V, d), float("nan"), device=dev).to(torch.bfloat16))
 
 
-def _check_pair(T, d, V, dtype, seed, reduction, accumulate):
-    log(f"scratch call T={T} d={d} V={V} {dtype} {reduction} acc={accumulate}")
+def _check_pair(T, d, V, dtype, seed, reduction, accumulate, gather=False):
+    log(f"scratch call T={T} d={d} V={V} {dtype} {reduction} acc={accumulate} gather={gather}")
     inp = wl.make_inputs(T, d, V, dtype, seed=seed, sigma_w=0.3, ignore_frac=0.1)
     H, W, y = device_inputs(inp)
     plan = flce.flce_plan(T, d, V, dtype, CAP)
+    if gather:
+        plan = gather_plan(plan)
     assert plan.ws_bytes <= flce.FLCE_SCRATCH_BYTES
     dev = W.device
     base = torch.randn((V, d), device=dev, generator=torch.Generator(dev).manual_seed(seed))
@@ -70,7 +72,7 @@ def test_scratch_call_matches_workspace_call(dtype):
     p1 = _check_pair(6000, 1024 if dtype == wl.DTYPE_BF16 else 512, 30000, dtype, 71,
                      "mean_valid", False)
     assert p1.n_slabs >= 2 or p1.n_blocks >= 2
-    _check_pair(700, 256, 5000, dtype, 72, "sum", True)
+    _check_pair(700, 256, 5000, dtype, 72, "sum", True, gather=True)
 
 
 def test_scratch_call_refuses_a_large_plan():
