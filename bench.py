@@ -792,6 +792,9 @@ def main():
                    "targets": cfg.targets, "ignored_tokens": cfg.n_ignored,
                    "grad_scale": gs, "parallelism": "single GPU"},
         "mfma_peak_frac": round(value / peak, 4),
+        # the build's target for this workload: 60% of the dense MFMA peak
+        "target_mfma_peak_frac": 0.6,
+        "target_met": bool(value / peak >= 0.6),
         # 2*T*d*V + 6*T_valid*d*V per step: the work left once the backward
         # skips ignored tokens (equal to value when none are ignored)
         "effective_tflops": round(effective, 2),
