@@ -183,7 +183,9 @@ typedef enum {
  *   dW [V x d] float: overwritten, or accumulated into when accumulate_dW
  *       != 0 (the fp32 main gradient across micro-batches).
  *   dW_bf16 : NULL, or [V x d] bf16 that receives dW rounded to nearest
- *       even after the call's accumulation.
+ *       even after the call's accumulation.  The dW tiles of the last token
+ *       block that holds a non-ignored token write it as they store the final
+ *       dW, so it costs no pass over dW of its own (except when T == 0).
  *   ws, ws_bytes : at least plan->ws_bytes.
  * Errors as flce_forward / flce_backward, and FLCE_ERR_INVALID_ARG for an
  * unknown reduction.  Outputs equal flce_forward then flce_backward with the

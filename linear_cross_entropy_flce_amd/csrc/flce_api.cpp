@@ -314,8 +314,8 @@ flce_status_t forward_impl(const flce_plan_t* plan, const void* H, const void* W
 // and tg.total = V); lse is over the whole vocabulary.
 flce_status_t backward_impl(const flce_plan_t* plan, const void* H, const void* W,
                             const flce::Targets& tg, const float* lse, float grad_scale,
-                            const float* g_dev, void* dH, float* dW, int accumulate_dW, void* ws,
-                            uint64_t ws_bytes, void* stream) {
+                            const float* g_dev, void* dH, float* dW, int accumulate_dW,
+                            void* dW_bf16, void* ws, uint64_t ws_bytes, void* stream) {
   flce_status_t st = check_plan(plan);
   if (st != FLCE_OK) return st;
   const flce_plan_t& p = *plan;
@@ -337,6 +337,13 @@ flce_status_t backward_impl(const flce_plan_t* plan, const void* H, const void* 
       e = flce::launch_fill_zero(dW, p.V * p.d, s);
       tm.done();
       if (e != hipSuccess) return hip_fail(e, "dW fill launch");
+    }
+    if (dW_bf16) {
+      // no dW tile runs: the copy takes a pass of its own
+      Timed tm(s, K_CAST, 0, p.V * p.d * 6.0);
+      e = flce::launch_cast_bf16(dW, dW_bf16, p.V * p.d, s);
+      tm.done();
+      if (e != hipSuccess) return hip_fail(e, "dW cast launch");
     }
     return ok();
   }
@@ -429,6 +436,7 @@ flce_status_t backward_impl(const flce_plan_t* plan, const void* H, const void* 
       w.n_ntiles = (int)cdiv(v_count, ti.dw_bn);
       w.accumulate = (b > 0 || accumulate_dW) ? 1 : 0;
       w.dW = dW;
+      w.dW_bf16 = dW_bf16;
       // dH and dW in one launch (both only read this slab's dZ)
       Timed t_hw(s, K_BWD_DHDW, 4.0 * tc * dd * vc,
                  2.0 * tc * vc * esz + vc * dd * esz +
@@ -639,8 +647,8 @@ flce_status_t flce_backward(const flce_plan_t* plan, const void* H, const void* 
   const flce_status_t st = check_plan(plan);
   if (st != FLCE_OK) return st;
   const flce::Targets tg{y, ignore_index, 0, plan->V};
-  return backward_impl(plan, H, W, tg, lse, grad_scale, nullptr, dH, dW, accumulate_dW, ws,
-                       ws_bytes, stream);
+  return backward_impl(plan, H, W, tg, lse, grad_scale, nullptr, dH, dW, accumulate_dW, nullptr,
+                       ws, ws_bytes, stream);
 }
 
 flce_status_t flce_forward_backward(const flce_plan_t* plan, const void* H, const void* W,
@@ -682,16 +690,9 @@ flce_status_t flce_forward_backward(const flce_plan_t* plan, const void* H, cons
     e = launch_loss_sum(loss, 0, scale, loss_reduced, s);
     if (e != hipSuccess) return hip_fail(e, "loss_sum launch");
   }
-  st = backward_impl(plan, H, W, tg, lse, scale, g_dev, dH, dW, accumulate_dW, ws, ws_bytes,
-                     stream);
-  if (st != FLCE_OK) return st;
-  if (dW_bf16) {
-    Timed tm(s, K_CAST, 0, p.V * p.d * 6.0);
-    e = flce::launch_cast_bf16(dW, dW_bf16, p.V * p.d, s);
-    tm.done();
-    if (e != hipSuccess) return hip_fail(e, "dW cast launch");
-  }
-  return ok();
+  // the last block with tokens writes the bf16 copy of dW from its dW tiles
+  return backward_impl(plan, H, W, tg, lse, scale, g_dev, dH, dW, accumulate_dW, dW_bf16, ws,
+                       ws_bytes, stream);
 }
 
 flce_status_t flce_forward_backward_scratch(const flce_plan_t* plan, const void* H,
@@ -780,7 +781,7 @@ flce_status_t flce_backward_shard(const flce_plan_t* plan, const void* H, const 
   if (st != FLCE_OK) return st;
   const flce::Targets tg{y, ignore_index, vocab_start, vocab_total};
   return backward_impl(plan, H, W_shard, tg, lse, grad_scale, nullptr, dH_partial, dW_shard,
-                       accumulate_dW, ws, ws_bytes, stream);
+                       accumulate_dW, nullptr, ws, ws_bytes, stream);
 }
 
 flce_status_t flce_token_logprobs(int64_t T, int64_t d, int64_t V, flce_dtype_t dtype,

@@ -27,11 +27,13 @@
 //                dH_block (+)= dZ W_slab   (fp32 accumulate, cast at the end;
 //                the slab's K loop cut into parts when the block has too few
 //                tiles to occupy the GPU), and
-//                dW_slab^T (+)= H_block^T dZ (fp32, deterministic block order).
+//                dW_slab^T (+)= H_block^T dZ (fp32, deterministic block order);
+//                the last block holding tokens also writes the optional bf16
+//                copy of dW from the same tiles.
 //   bwd_dh_reduce  sums dH's parts in order and applies the accumulator mode.
 //   token_logit  gathered h . w minus lse for given tokens (scoring), up to
 //                eight gathered rows per pass.
-//   cast_bf16    optional bf16 copy of dW.
+//   cast_bf16    the bf16 copy of dW when no dW tile runs (T = 0).
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -153,6 +155,13 @@ struct DwCfg<float> {
 __device__ __forceinline__ int block_count(const TokBlock& b) {
   const int64_t n = (int64_t)*b.tv - b.t_begin;
   return n <= 0 ? 0 : (n < b.t_max ? (int)n : b.t_max);
+}
+
+// The last block that holds a non-ignored token (block 0 when there is none):
+// the one whose dW is final for the whole call.
+__device__ __forceinline__ bool last_filled_block(const TokBlock& b) {
+  const int64_t tv = *b.tv;
+  return tv == 0 ? b.t_begin == 0 : (b.t_begin < tv && tv <= b.t_begin + b.t_max);
 }
 
 __device__ __forceinline__ uint32_t clamp_bytes(int64_t b) {
@@ -808,7 +817,13 @@ __device__ __forceinline__ void dw_body(const DwArgs& a, int bid, char* lds) {
   const int64_t vl0 = (int64_t)tn * TL::BN;  // vocab within slab
 
   const int t_count = block_count(a.blk);  // K
-  if (t_count == 0 && a.accumulate) return;  // nothing to add
+  // the bf16 copy comes from the block whose dW is final
+  __bf16* dwb = a.dW_bf16 != nullptr && last_filled_block(a.blk)
+                    ? reinterpret_cast<__bf16*>(a.dW_bf16) + (a.v_begin + vl0) * a.d + n0
+                    : nullptr;
+  // nothing to add; an empty block that still owes the copy rewrites its
+  // tile of dW unchanged below
+  if (t_count == 0 && a.accumulate && dwb == nullptr) return;
 
   Operand A, B;
   A.rs = make_rsrc(a.Ht, clamp_bytes((int64_t)a.d * a.ldht * ESZ));
@@ -850,10 +865,14 @@ __device__ __forceinline__ void dw_body(const DwArgs& a, int bid, char* lds) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int row = TL::row_of(wm, i, 4 * q);
-        if (row < n_rows)
-          *reinterpret_cast<f32x4_t*>(dw + (int64_t)c * a.d + row) =
-              f32x4_t{tile.acc[i][j][4 * q], tile.acc[i][j][4 * q + 1], tile.acc[i][j][4 * q + 2],
-                      tile.acc[i][j][4 * q + 3]};
+        if (row < n_rows) {
+          const f32x4_t v = {tile.acc[i][j][4 * q], tile.acc[i][j][4 * q + 1],
+                             tile.acc[i][j][4 * q + 2], tile.acc[i][j][4 * q + 3]};
+          *reinterpret_cast<f32x4_t*>(dw + (int64_t)c * a.d + row) = v;
+          if (dwb != nullptr)
+            *reinterpret_cast<bf16x4_t*>(dwb + (int64_t)c * a.d + row) =
+                bf16x4_t{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+        }
       }
   }
 }

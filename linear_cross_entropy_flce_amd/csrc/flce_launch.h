@@ -111,6 +111,10 @@ struct DwArgs {
   int n_mtiles, n_ntiles;  // hidden tiles, vocab tiles
   int accumulate;
   float* dW;
+  // When set, the last block holding any token (block 0 when none does) also
+  // writes the bf16 copy of its finished dW tiles here ([V][d], round to
+  // nearest even), so that the copy needs no pass of its own.
+  void* dW_bf16;
 };
 
 struct TileInfo {

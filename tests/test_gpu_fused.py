@@ -147,6 +147,65 @@ def test_dW_bf16_is_rounded_dW():
     assert np.array_equal(got, want)
 
 
+def _bf16_bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("dtype", [wl.DTYPE_F32, wl.DTYPE_BF16])
+@pytest.mark.parametrize("ign,acc", [(0.6, False), (0.6, True), (0.0, True), (1.0, False),
+                                     (1.0, True)])
+def test_dW_bf16_over_token_blocks(dtype, ign, acc):
+    """Six token blocks of 256 (a small workspace cap), the trailing ones
+    empty when most tokens are ignored, or all of them: the bf16 copy, which
+    the dW tiles of the last block holding tokens write (block 0 when none
+    does), is dW rounded to nearest even in every element, and dW equals the
+    separate calls' bit for bit."""
+    T, d, V = 1500, 64, 3000
+    inp = wl.make_inputs(T, d, V, dtype, seed=4100 + int(10 * ign) + acc, sigma_w=0.5,
+                         ignore_frac=ign)
+    H, W, y = device_inputs(inp)
+    plan = flce.flce_plan(T, d, V, dtype, 400_000)
+    n_valid = int((inp.y != IGN).sum())
+    log(f"  {plan.n_blocks} blocks of {plan.bwd_block}, {plan.n_slabs} slabs, "
+        f"{n_valid} tokens not ignored")
+    assert plan.n_blocks >= 3
+    base = np.random.default_rng(41).standard_normal((V, d)).astype(np.float32)
+    dW = torch.from_numpy(base).cuda() if acc else None
+    # NaN everywhere first, so that an element the kernels skip shows
+    dWb = torch.full((V, d), float("nan"), dtype=torch.bfloat16, device=W.device)
+    a = flce.flce_forward_backward(plan, H, W, y, IGN, "sum", 0.5, dW=dW, accumulate_dW=acc,
+                                   dW_bf16=dWb)
+    dW2 = torch.from_numpy(base).cuda() if acc else None
+    _, lse, _ = flce.flce_forward(plan, H, W, y, IGN, 0.5)
+    _, dW2 = flce.flce_backward(plan, H, W, y, lse, IGN, 0.5, dW=dW2, accumulate_dW=acc)
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(a["dW"]), _np(dW2))
+    assert np.array_equal(_bf16_bits(dWb), wl.f32_to_bf16_bits(_np(a["dW"])))
+    if n_valid == 0:
+        assert np.array_equal(_np(a["dW"]), base if acc else np.zeros_like(base))
+
+
+@pytest.mark.parametrize("acc", [False, True])
+def test_dW_bf16_without_tokens(acc):
+    """T = 0: no dW tile runs, so the copy takes a pass of its own; it is the
+    caller's dW rounded (accumulating) or zeros."""
+    d, V = 64, 1000
+    dev = torch.device("cuda:0")
+    H = torch.empty((0, d), dtype=torch.bfloat16, device=dev)
+    W = torch.randn((V, d), device=dev).to(torch.bfloat16)
+    y = torch.empty(0, dtype=torch.int64, device=dev)
+    plan = flce.flce_plan(0, d, V, wl.DTYPE_BF16)
+    base = torch.randn((V, d), device=dev)
+    dW = base.clone()
+    dWb = torch.full((V, d), float("nan"), dtype=torch.bfloat16, device=dev)
+    flce.flce_forward_backward(plan, H, W, y, IGN, "sum", 1.0, dW=dW, accumulate_dW=acc,
+                               dW_bf16=dWb)
+    torch.cuda.synchronize()
+    want = base if acc else torch.zeros_like(base)
+    assert torch.equal(dW, want)
+    assert np.array_equal(_bf16_bits(dWb), wl.f32_to_bf16_bits(_np(want)))
+
+
 @pytest.mark.parametrize("dtype", [wl.DTYPE_F32, wl.DTYPE_BF16])
 def test_micro_batch_accumulation(dtype):
     """Two micro-batches, the second accumulating into the first's fp32 dW,
