@@ -587,6 +587,67 @@ def library_gemm_leg(reps: int = 10):
     return out
 
 
+TIMELINE_LAUNCH = {1: "fwd_sweep", 2: "bwd_dz", 3: "bwd_dhdw", 4: "bwd_dhdw"}
+
+
+def summarize_timeline(records) -> dict:
+    """Splits each launch's compute-unit time into the workgroups' own time
+    (busy), the time before a unit's first workgroup (head), between its
+    consecutive workgroups (turnover) and after its last one until the launch's
+    last workgroup ends (tail).  records: flce_wg_record_t-like objects (hw_id,
+    xcc_id, t_start, t_end, kernel) from libflce_timeline.so.  A launch is a
+    maximal run of records of one kernel in start order (the step's launches
+    alternate kernels); stamps tick at 100 MHz."""
+    import numpy as np
+    if not records:
+        return {"records": 0}
+    hw = np.array([r.hw_id for r in records], np.int64)
+    xcc = np.array([r.xcc_id for r in records], np.int64) & 0xF
+    cu = xcc * 1000 + ((hw >> 13) & 7) * 100 + ((hw >> 12) & 1) * 50 + ((hw >> 8) & 15)
+    t0 = np.array([r.t_start for r in records], np.int64)
+    t1 = np.array([r.t_end for r in records], np.int64)
+    kern = np.array([r.kernel for r in records], np.int64)
+    name = np.array([TIMELINE_LAUNCH.get(int(k), "other") for k in kern])
+    order = np.argsort(t0, kind="stable")
+    cu, t0, t1, kern, name = cu[order], t0[order], t1[order], kern[order], name[order]
+    n_cu = len(np.unique(cu))
+    cuts = np.flatnonzero(name[1:] != name[:-1]) + 1
+    out = {}
+    for seg in np.split(np.arange(len(t0)), cuts):
+        k = str(name[seg[0]])
+        a, b = int(t0[seg].min()), int(t1[seg].max())
+        acc = out.setdefault(k, dict(launches=0, workgroups=0, cu_time=0, busy=0, head=0,
+                                     turnover=0, tail=0, durations={}))
+        acc["launches"] += 1
+        acc["workgroups"] += len(seg)
+        acc["cu_time"] += (b - a) * n_cu
+        for c in np.unique(cu[seg]):
+            m = seg[cu[seg] == c]
+            m = m[np.argsort(t0[m], kind="stable")]
+            acc["busy"] += int((t1[m] - t0[m]).sum())
+            acc["head"] += int(t0[m[0]] - a)
+            acc["tail"] += int(b - t1[m[-1]])
+            acc["turnover"] += int(np.clip(t0[m[1:]] - t1[m[:-1]], 0, None).sum())
+        for kk in np.unique(kern[seg]):
+            sel = seg[kern[seg] == kk]
+            acc["durations"].setdefault(int(kk), []).extend((t1[sel] - t0[sel]).tolist())
+    res = {"records": len(records), "compute_units": n_cu, "tick_ns": 10,
+           "shares": "of the launches' compute-unit time (span x compute units)", "kernels": {}}
+    for k, acc in out.items():
+        ct = max(acc["cu_time"], 1)
+        e = {"launches": acc["launches"], "workgroups": acc["workgroups"],
+             "busy": round(acc["busy"] / ct, 4), "head": round(acc["head"] / ct, 4),
+             "turnover": round(acc["turnover"] / ct, 4), "tail": round(acc["tail"] / ct, 4)}
+        for kk, dur in sorted(acc["durations"].items()):
+            d = np.array(dur, np.float64) / 100.0  # microseconds
+            tag = {3: "dH_", 4: "dW_"}.get(kk, "")
+            e[tag + "wg_us"] = {"median": round(float(np.median(d)), 2),
+                                "p5": round(float(np.percentile(d, 5)), 2),
+                                "p95": round(float(np.percentile(d, 95)), 2)}
+        res["kernels"][k] = e
+    return res
+
+
 def copy_calibration(mib: int):
     """A plain copy of mib MiB (read mib, write mib), three times: the byte
     counters of a profiler run over it give the scale of FETCH_SIZE and
@@ -629,6 +690,10 @@ def main():
                          "is data-dependent power")
     ap.add_argument("--library-gemm", action="store_true",
                     help="also time the block/slab GEMM shapes as plain torch.matmul (hipBLASLt)")
+    ap.add_argument("--timeline", action="store_true",
+                    help="only run the warm-up and one step in libflce_timeline.so (the same "
+                         "kernels with per-workgroup stamps) and print how each kernel's "
+                         "compute-unit time splits into workgroups, turnover gaps and tails")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this many MiB (a known-size "
                          "reference for the HBM byte counters) and exit")
@@ -666,7 +731,10 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(3)
-    flce.load()
+    if args.timeline:
+        flce.load(flce.TIMELINE_LIB_PATH)
+    else:
+        flce.load()
     torch.cuda.init()
     free_before = torch.cuda.mem_get_info()[0]  # hipMemGetInfo before any of the step's buffers
     if args.shape:
@@ -715,6 +783,19 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.timeline:
+        flce.flce_timeline_reset()
+        log("one step with workgroup stamps")
+        step()
+        torch.cuda.synchronize()
+        tl = summarize_timeline(flce.flce_timeline_read())
+        tl["workload"] = cfg.name
+        for k, e in tl.get("kernels", {}).items():
+            log(f"  {k:10s} launches {e['launches']:4d} workgroups {e['workgroups']:7d}: busy "
+                f"{100 * e['busy']:5.1f}%  head {100 * e['head']:4.1f}%  turnover "
+                f"{100 * e['turnover']:4.1f}%  tail {100 * e['tail']:4.1f}%")
+        print(json.dumps(tl))
+        return
     torch.cuda.reset_peak_memory_stats()
     flce.flce_timing_collect()  # discard anything recorded so far
     flce.flce_timing_enable(True)

@@ -328,6 +328,34 @@ flce_status_t flce_timing_enable(int enable);
  * event query fails. */
 flce_status_t flce_timing_collect(flce_kernel_time_t* out, int max_entries, int* n_out);
 
+/* ---- workgroup timeline (a profiling aid of a separate build) ------------
+ * Not part of the method; no passage of the pages defines it.  In the library
+ * built with -DFLCE_TIMELINE=1 (libflce_timeline.so, compiled by the build
+ * step beside libflce.so), every workgroup of the forward sweep, the dZ
+ * recompute and the dH/dW launch appends one record: the compute unit it ran
+ * on and two stamps of the GPU's constant 100 MHz real-time counter, taken
+ * at its start and after its last store was issued.  The record holds up to
+ * 524,288 workgroups; later ones are counted but dropped.  In libflce.so both
+ * calls return FLCE_ERR_UNSUPPORTED and touch nothing. */
+typedef struct {
+  uint32_t hw_id;    /* the HW_ID register: CU_ID in bits 11:8, SH_ID bit 12, SE_ID 15:13 */
+  uint32_t xcc_id;   /* the XCC_ID register: the XCD in bits 3:0 */
+  uint64_t t_start;  /* real-time counter at the workgroup's start */
+  uint64_t t_end;    /* ... after its last store was issued */
+  uint32_t kernel;   /* 1 forward sweep, 2 dZ recompute, 3 dH and 4 dW workgroups of bwd_dhdw */
+  uint32_t block;    /* the workgroup's index in its launch */
+} flce_wg_record_t;
+
+/* Clears the record (a synchronous copy to the device).  FLCE_ERR_HIP when
+ * the copy fails. */
+flce_status_t flce_timeline_reset(void);
+
+/* Waits for the device, then copies up to max_records records in the order
+ * the workgroups finished into out (host memory) and writes their number to
+ * *n_out.  FLCE_ERR_INVALID_ARG for NULL pointers, FLCE_ERR_HIP when a copy
+ * fails. */
+flce_status_t flce_timeline_read(flce_wg_record_t* out, int max_records, int* n_out);
+
 /* Static description of a status code. */
 const char* flce_status_string(flce_status_t status);
 

@@ -32,7 +32,12 @@ EXPORTED = ["flce_plan", "flce_forward", "flce_backward", "flce_forward_backward
             "flce_forward_backward_scratch",
             "flce_forward_shard",
             "flce_merge_shards", "flce_backward_shard", "flce_token_logprobs", "flce_timing_enable",
-            "flce_timing_collect", "flce_status_string", "flce_last_error", "flce_version"]
+            "flce_timing_collect", "flce_timeline_reset", "flce_timeline_read",
+            "flce_status_string", "flce_last_error", "flce_version"]
+# libflce_timeline.so: the same library with the per-workgroup timeline
+TIMELINE_LIB_PATH = os.path.join(PKG, "libflce_timeline.so")
+# flce_wg_record_t.kernel
+TIMELINE_KERNELS = {1: "fwd_sweep", 2: "bwd_dz", 3: "bwd_dhdw:dH", 4: "bwd_dhdw:dW"}
 
 
 class Plan(ctypes.Structure):
@@ -60,6 +65,13 @@ class KernelTime(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 24), ("launches", ctypes.c_int64),
                 ("total_ms", ctypes.c_double), ("flops", ctypes.c_double),
                 ("bytes", ctypes.c_double)]
+
+
+class WgRecord(ctypes.Structure):
+    """Mirror of flce_wg_record_t."""
+    _fields_ = [("hw_id", ctypes.c_uint32), ("xcc_id", ctypes.c_uint32),
+                ("t_start", ctypes.c_uint64), ("t_end", ctypes.c_uint64),
+                ("kernel", ctypes.c_uint32), ("block", ctypes.c_uint32)]
 
 
 class FlceError(RuntimeError):
@@ -109,6 +121,11 @@ def load(path: str = LIB_PATH):
     lib.flce_timing_collect.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int,
                                         ctypes.POINTER(ctypes.c_int)]
     lib.flce_timing_collect.restype = ctypes.c_int
+    lib.flce_timeline_reset.argtypes = []
+    lib.flce_timeline_reset.restype = ctypes.c_int
+    lib.flce_timeline_read.argtypes = [ctypes.POINTER(WgRecord), ctypes.c_int,
+                                       ctypes.POINTER(ctypes.c_int)]
+    lib.flce_timeline_read.restype = ctypes.c_int
     lib.flce_status_string.argtypes = [ctypes.c_int]
     lib.flce_status_string.restype = ctypes.c_char_p
     lib.flce_last_error.argtypes = []
@@ -176,6 +193,20 @@ def flce_timing_collect() -> dict:
     return {buf[i].name.decode(): dict(launches=buf[i].launches, total_ms=buf[i].total_ms,
                                        flops=buf[i].flops, bytes=buf[i].bytes)
             for i in range(n.value)}
+
+
+def flce_timeline_reset() -> None:
+    """flce_timeline_reset(): raises FlceError (FLCE_ERR_UNSUPPORTED) unless the
+    loaded library is libflce_timeline.so."""
+    _check(load().flce_timeline_reset())
+
+
+def flce_timeline_read(max_records: int = 1 << 19):
+    """flce_timeline_read(): the records as a list of WgRecord."""
+    buf = (WgRecord * max_records)()
+    n = ctypes.c_int(0)
+    _check(load().flce_timeline_read(buf, max_records, ctypes.byref(n)))
+    return buf[:n.value]
 
 
 def flce_plan(T: int, d: int, V: int, dtype, vocab_ws_cap_bytes: int = 0) -> Plan:

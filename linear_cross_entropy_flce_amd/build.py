@@ -1,4 +1,6 @@
-"""Builds libflce.so (HIP kernels + C-ABI) for gfx950 with hipcc, in-tree.
+"""Builds libflce.so (HIP kernels + C-ABI) for gfx950 with hipcc, in-tree,
+and libflce_timeline.so, the same sources with the per-workgroup timeline of
+the main kernels compiled in (a profiling aid; bench.py --timeline).
 
 Usage: python -m linear_cross_entropy_flce_amd.build [--verbose]
 """
@@ -13,6 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libflce.so")
+TIMELINE_LIB = os.path.join(PKG, "libflce_timeline.so")
 SOURCES = ["flce_kernels.hip", "flce_api.cpp"]
 ARCH = os.environ.get("FLCE_OFFLOAD_ARCH", "gfx950")
 
@@ -52,6 +55,15 @@ def build(verbose: bool = False, extra=(), out: str = LIB) -> str:
     return out
 
 
+def build_all(verbose: bool = False) -> list:
+    """libflce.so, then libflce_timeline.so."""
+    return [build(verbose=verbose),
+            build(verbose=verbose, extra=["-DFLCE_TIMELINE=1"], out=TIMELINE_LIB)]
+
+
 if __name__ == "__main__":
     extra = [a for a in sys.argv[1:] if a != "--verbose"]
-    print(build(verbose="--verbose" in sys.argv, extra=extra))
+    if extra:
+        print(build(verbose="--verbose" in sys.argv, extra=extra))
+    else:
+        print("\n".join(build_all(verbose="--verbose" in sys.argv)))

@@ -5,6 +5,7 @@
 // reproducible bit for bit.
 #include <hip/hip_runtime_api.h>
 #include <stdarg.h>
+#include <stddef.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <string.h>
@@ -501,6 +502,28 @@ flce_status_t flce_timing_collect(flce_kernel_time_t* out, int max_entries, int*
   return st == FLCE_OK ? ok() : st;
 }
 
+
+flce_status_t flce_timeline_reset(void) {
+  const hipError_t e = flce::timeline_reset();
+  if (e == hipErrorNotSupported)
+    return fail(FLCE_ERR_UNSUPPORTED, "this library was built without the workgroup timeline");
+  if (e != hipSuccess) return hip_fail(e, "timeline reset");
+  return ok();
+}
+
+flce_status_t flce_timeline_read(flce_wg_record_t* out, int max_records, int* n_out) {
+  if (!out || !n_out) return fail(FLCE_ERR_INVALID_ARG, "out and n_out must be non-NULL");
+  static_assert(sizeof(flce_wg_record_t) == sizeof(flce::TimelineRecord) &&
+                    offsetof(flce_wg_record_t, t_start) == offsetof(flce::TimelineRecord, t_start) &&
+                    offsetof(flce_wg_record_t, kernel) == offsetof(flce::TimelineRecord, kernel),
+                "one record layout");
+  const hipError_t e =
+      flce::timeline_read(reinterpret_cast<flce::TimelineRecord*>(out), max_records, n_out);
+  if (e == hipErrorNotSupported)
+    return fail(FLCE_ERR_UNSUPPORTED, "this library was built without the workgroup timeline");
+  if (e != hipSuccess) return hip_fail(e, "timeline read");
+  return ok();
+}
 
 const char* flce_version(void) { return "0.1.0"; }
 

@@ -157,6 +157,53 @@ __device__ __forceinline__ int block_count(const TokBlock& b) {
   return n <= 0 ? 0 : (n < b.t_max ? (int)n : b.t_max);
 }
 
+// ------------------------------------------------------ workgroup timeline
+// Profiling build only (-DFLCE_TIMELINE=1, libflce_timeline.so): each
+// workgroup of the forward sweep, the dZ recompute and the dH/dW launch
+// records the compute unit it ran on (HW_ID and XCC_ID registers) and
+// wall-clock stamps (the 100 MHz real-time counter) at its start and after
+// its last store was issued, so that a launch's compute-unit time can be
+// split into workgroups, the gaps between them and the launch's tail.  In
+// the default build the stamps compile to nothing.
+#ifndef FLCE_TIMELINE
+#define FLCE_TIMELINE 0
+#endif
+#if FLCE_TIMELINE
+constexpr unsigned kTimelineCap = 1u << 19;
+__device__ TimelineRecord g_timeline[kTimelineCap];
+__device__ unsigned int g_timeline_n;
+#endif
+
+__device__ __forceinline__ uint64_t timeline_start() {
+#if FLCE_TIMELINE
+  return wall_clock64();
+#else
+  return 0;
+#endif
+}
+
+__device__ __forceinline__ void timeline_end(uint32_t kernel, uint64_t t_start) {
+#if FLCE_TIMELINE
+  if (threadIdx.x == 0) {
+    const uint64_t t_end = wall_clock64();
+    const unsigned slot = atomicAdd(&g_timeline_n, 1u);
+    if (slot < kTimelineCap) {
+      TimelineRecord r;
+      r.hw_id = __builtin_amdgcn_s_getreg((31 << 11) | 4);    // HW_REG_HW_ID, 32 bits
+      r.xcc_id = __builtin_amdgcn_s_getreg((31 << 11) | 20);  // HW_REG_XCC_ID, 32 bits
+      r.t_start = t_start;
+      r.t_end = t_end;
+      r.kernel = kernel;
+      r.block = blockIdx.x;
+      g_timeline[slot] = r;
+    }
+  }
+#else
+  (void)kernel;
+  (void)t_start;
+#endif
+}
+
 // The last block that holds a non-ignored token (block 0 when there is none):
 // the one whose dW is final for the whole call.
 __device__ __forceinline__ bool last_filled_block(const TokBlock& b) {
@@ -193,6 +240,7 @@ __global__ void __launch_bounds__(LogitCfg<E>::T::NT, 1)
   using TL = typename LogitCfg<E>::T;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   constexpr int ESZ = TL::ESZ;
+  const uint64_t tl_t0 = timeline_start();
 
   // ---- workgroup -> (token tile, split)
   const int bid = blockIdx.x;
@@ -338,6 +386,7 @@ __global__ void __launch_bounds__(LogitCfg<E>::T::NT, 1)
     a.part[((int64_t)split * a.T + t) * 2 + 0] = M;
     a.part[((int64_t)split * a.T + t) * 2 + 1] = S;
   }
+  timeline_end(kTimelineFwdSweep, tl_t0);
 }
 
 // ============================================================== forward merge
@@ -618,9 +667,11 @@ __device__ __forceinline__ void dz_tile(const DzArgs& a, int tm, int tn, char* l
 template <typename E>
 __global__ void __launch_bounds__(LogitCfg<E>::T::NT, 1) bwd_dz_kernel(DzArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
+  const uint64_t tl_t0 = timeline_start();
   int tm, tn;
   if (!xcd_tile(blockIdx.x, a.n_vtiles, a.n_ttiles, 4, tm, tn)) return;
   dz_tile<E>(a, tm, tn, lds);
+  timeline_end(kTimelineDz, tl_t0);
 }
 
 // ================================================================ backward dH
@@ -887,8 +938,14 @@ __global__ void __launch_bounds__(DhCfg<E>::T::NT, 1) bwd_dhdw_kernel(DhArgs h, 
   static_assert(DhCfg<E>::T::NT == DwCfg<E>::T::NT &&
                 DhCfg<E>::T::LDS_BYTES == DwCfg<E>::T::LDS_BYTES, "one launch shape");
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  if ((int)blockIdx.x < dh_grid) dh_body<E>(h, blockIdx.x, lds);
-  else dw_body<E>(w, blockIdx.x - dh_grid, lds);
+  const uint64_t tl_t0 = timeline_start();
+  if ((int)blockIdx.x < dh_grid) {
+    dh_body<E>(h, blockIdx.x, lds);
+    timeline_end(kTimelineDh, tl_t0);
+  } else {
+    dw_body<E>(w, blockIdx.x - dh_grid, lds);
+    timeline_end(kTimelineDw, tl_t0);
+  }
 }
 
 __global__ void __launch_bounds__(256) fill_zero_kernel(float* p, int64_t n) {
@@ -1309,6 +1366,37 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
   return hipGetLastError();
+}
+
+// ========================================================= workgroup timeline
+hipError_t timeline_reset() {
+#if FLCE_TIMELINE
+  const unsigned zero = 0;
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_timeline_n), &zero, sizeof zero);
+#else
+  return hipErrorNotSupported;
+#endif
+}
+
+hipError_t timeline_read(TimelineRecord* out, int max_records, int* n_out) {
+#if FLCE_TIMELINE
+  *n_out = 0;
+  hipError_t e = hipDeviceSynchronize();
+  unsigned n = 0;
+  if (e == hipSuccess) e = hipMemcpyFromSymbol(&n, HIP_SYMBOL(g_timeline_n), sizeof n);
+  if (e != hipSuccess) return e;
+  if (n > kTimelineCap) n = kTimelineCap;  // the count runs on past a full buffer
+  if (max_records < 0) max_records = 0;
+  if (n > (unsigned)max_records) n = (unsigned)max_records;
+  if (n > 0) e = hipMemcpyFromSymbol(out, HIP_SYMBOL(g_timeline), (size_t)n * sizeof(TimelineRecord));
+  if (e == hipSuccess) *n_out = (int)n;
+  return e;
+#else
+  (void)out;
+  (void)max_records;
+  *n_out = 0;
+  return hipErrorNotSupported;
+#endif
 }
 
 // ============================================================= scratch array

@@ -117,6 +117,18 @@ struct DwArgs {
   void* dW_bf16;
 };
 
+// One workgroup of the profiling build's timeline (the layout of
+// flce_wg_record_t in flce.h).
+struct TimelineRecord {
+  uint32_t hw_id, xcc_id;
+  uint64_t t_start, t_end;
+  uint32_t kernel, block;
+};
+constexpr uint32_t kTimelineFwdSweep = 1, kTimelineDz = 2, kTimelineDh = 3, kTimelineDw = 4;
+// hipErrorNotSupported unless built with FLCE_TIMELINE=1
+hipError_t timeline_reset();
+hipError_t timeline_read(TimelineRecord* out, int max_records, int* n_out);
+
 struct TileInfo {
   // logits: vocab x tokens; dH: tokens x hidden; dW: hidden x vocab
   int logit_bm, logit_bn, dh_bm, dh_bn, dw_bm, dw_bn;

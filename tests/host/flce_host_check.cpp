@@ -96,6 +96,12 @@ hipError_t scratch_address(void** out) {
   return hipSuccess;
 }
 int dh_split_slots() { return 256; }
+// the default build: no workgroup timeline
+hipError_t timeline_reset() { return hipErrorNotSupported; }
+hipError_t timeline_read(TimelineRecord*, int, int* n_out) {
+  *n_out = 0;
+  return hipErrorNotSupported;
+}
 
 static double esz(bool bf16) { return bf16 ? 2.0 : 4.0; }
 
@@ -428,6 +434,12 @@ int main() {
   flce_plan_t pl;
   expect(flce_plan(10, 128, 1000, FLCE_BF16, 0, nullptr) == FLCE_ERR_INVALID_ARG, "NULL out");
   expect(flce_plan(10, 128, 1000, (flce_dtype_t)9, 0, &pl) == FLCE_ERR_INVALID_ARG, "bad dtype");
+  // the timeline calls of a library built without it
+  flce_wg_record_t recs[2];
+  int got = -1;
+  expect(flce_timeline_reset() == FLCE_ERR_UNSUPPORTED, "timeline reset");
+  expect(flce_timeline_read(recs, 2, &got) == FLCE_ERR_UNSUPPORTED && got == 0, "timeline read");
+  expect(flce_timeline_read(nullptr, 2, &got) == FLCE_ERR_INVALID_ARG, "timeline read NULL");
   printf("CASES %d FAILURES %d\n", n, g_fail);
   return g_fail ? 1 : 0;
 }

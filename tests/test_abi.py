@@ -45,6 +45,48 @@ def test_library_exports_every_declared_symbol(lib):
         assert getattr(lib, name) is not None
 
 
+def test_timeline_is_absent_from_the_default_library(lib):
+    """libflce.so is built without the workgroup timeline: both calls say so
+    and touch nothing (no device call is made)."""
+    assert lib.flce_timeline_reset() == flce.FLCE_ERR_UNSUPPORTED
+    buf = (flce.WgRecord * 4)()
+    n = ctypes.c_int(-1)
+    assert lib.flce_timeline_read(buf, 4, ctypes.byref(n)) == flce.FLCE_ERR_UNSUPPORTED
+    assert n.value == 0
+    assert lib.flce_timeline_read(None, 4, ctypes.byref(n)) == flce.FLCE_ERR_INVALID_ARG
+    assert lib.flce_timeline_read(buf, 4, None) == flce.FLCE_ERR_INVALID_ARG
+
+
+def test_timeline_library_exports_every_declared_symbol():
+    """libflce_timeline.so (the profiling build) has the same C-ABI."""
+    path = flce.TIMELINE_LIB_PATH
+    if not os.path.exists(path):
+        from linear_cross_entropy_flce_amd import build
+        build.build(extra=["-DFLCE_TIMELINE=1"], out=path)
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    syms = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for name in declared_functions():
+        assert name in syms, name
+
+
+def test_timeline_record_layout_matches_header(tmp_path):
+    """The ctypes mirror of flce_wg_record_t has the C compiler's layout."""
+    fields = [f for f, _ in flce.WgRecord._fields_]
+    src = tmp_path / "wg.c"
+    src.write_text("#include <stddef.h>\n#include <stdio.h>\n#include \"flce.h\"\n"
+                   "int main(void) {\n  printf(\"%zu\\n\", sizeof(flce_wg_record_t));\n" +
+                   "".join(f"  printf(\"%zu\\n\", offsetof(flce_wg_record_t, {f}));\n"
+                           for f in fields) + "  return 0;\n}\n")
+    exe = tmp_path / "wg"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(exe)], check=True)
+    out = [int(v) for v in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    assert out[0] == ctypes.sizeof(flce.WgRecord)
+    assert out[1:] == [getattr(flce.WgRecord, f).offset for f in fields]
+
+
 def test_plan_struct_layout_matches_header(tmp_path):
     """The ctypes mirror of flce_plan_t has the C compiler's size and field
     offsets (include/flce.h built as plain C99)."""

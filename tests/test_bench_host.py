@@ -155,3 +155,35 @@ def test_device_code_digest_of_a_broken_file_is_none(bench, tmp_path):
     assert bench.device_code_digest(str(tmp_path / "trunc.so")) is None
     assert bench.device_code_digest(str(tmp_path / "text.so")) is None
     assert bench.device_code_digest(str(tmp_path / "missing.so")) is None
+
+
+class _Rec:
+    def __init__(self, cu, t0, t1, kernel, xcc=0):
+        self.hw_id, self.xcc_id = cu << 8, xcc
+        self.t_start, self.t_end, self.kernel = t0, t1, kernel
+
+
+def test_summarize_timeline_splits_compute_unit_time(bench):
+    """Two compute units, a dZ launch then a dH/dW launch (stamps in ticks):
+    the shares are the hand-computed ones and sum to one per kernel."""
+    recs = [_Rec(0, 0, 100, 2), _Rec(0, 110, 200, 2), _Rec(1, 0, 150, 2),
+            _Rec(0, 300, 500, 3), _Rec(1, 300, 400, 4), _Rec(1, 405, 480, 4)]
+    tl = bench.summarize_timeline(recs)
+    assert tl["records"] == 6 and tl["compute_units"] == 2
+    dz, hw = tl["kernels"]["bwd_dz"], tl["kernels"]["bwd_dhdw"]
+    # dZ: span 200 x 2 units = 400; workgroups 340, a 10-tick gap, a 50-tick tail
+    assert (dz["launches"], dz["workgroups"]) == (1, 3)
+    assert (dz["busy"], dz["head"], dz["turnover"], dz["tail"]) == (0.85, 0.0, 0.025, 0.125)
+    # dH/dW: span 200 x 2 = 400; workgroups 375, a 5-tick gap, a 20-tick tail
+    assert (hw["busy"], hw["turnover"], hw["tail"]) == (0.9375, 0.0125, 0.05)
+    assert hw["dH_wg_us"]["median"] == 2.0 and hw["dW_wg_us"]["median"] == 0.88  # 0.875, rounded
+    for e in tl["kernels"].values():
+        assert abs(e["busy"] + e["head"] + e["turnover"] + e["tail"] - 1.0) < 1e-9
+
+
+def test_summarize_timeline_separates_units_of_different_xcds(bench):
+    """The same CU number on two XCDs is two compute units."""
+    recs = [_Rec(3, 0, 10, 2, xcc=0), _Rec(3, 0, 10, 2, xcc=1)]
+    tl = bench.summarize_timeline(recs)
+    assert tl["compute_units"] == 2 and tl["kernels"]["bwd_dz"]["busy"] == 1.0
+    assert bench.summarize_timeline([]) == {"records": 0}

@@ -17,16 +17,22 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-@pytest.fixture(scope="module")
-def asm(tmp_path_factory):
+def _compile(tmp_path_factory, extra=()):
     from linear_cross_entropy_flce_amd import build as b
-    flags = [f for f in b.flags() if f not in ("-fPIC", "-shared")]
+    flags = [f for f in b.flags(extra) if f not in ("-fPIC", "-shared")]
     out = tmp_path_factory.mktemp("asm") / "kernels.s"
     cmd = [b.hipcc(), *flags, "--cuda-device-only", "-S",
            os.path.join(b.CSRC, "flce_kernels.hip"), "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stderr[-2000:]
     return out.read_text()
+
+
+# the default build (libflce.so) and the profiling build with the workgroup
+# timeline (libflce_timeline.so) must both hold every property
+@pytest.fixture(scope="module", params=["default", "timeline"])
+def asm(request, tmp_path_factory):
+    return _compile(tmp_path_factory, ["-DFLCE_TIMELINE=1"] if request.param == "timeline" else [])
 
 
 def _kernels(text):
