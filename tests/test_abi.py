@@ -10,6 +10,8 @@ import re
 import subprocess
 
 import pytest
+from hypothesis import HealthCheck, given, settings
+from hypothesis import strategies as st
 
 import linear_cross_entropy_flce_amd as flce
 import workloads as wl
@@ -224,6 +226,39 @@ def test_plan_invariants_on_configs(lib, cfg):
     n_vt = -(-cfg.V // p.tile_v)
     assert p.fwd_splits * p.fwd_tiles_per_split >= n_vt
     assert (p.fwd_splits - 1) * p.fwd_tiles_per_split < n_vt
+    assert p.ws_bytes == max(p.fwd_ws_bytes, p.bwd_ws_bytes) + 256
+
+
+@settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.function_scoped_fixture])
+@given(T=st.integers(0, 300_000), d8=st.integers(1, 2048), V=st.integers(1, 300_000),
+       bf16=st.booleans(), cap=st.one_of(st.just(0), st.integers(100_000, 2_000_000_000)))
+def test_plan_invariants_hold_for_any_shape(lib, T, d8, V, bf16, cap):
+    """For any shape, dtype and cap the planner either refuses with
+    FLCE_ERR_WORKSPACE (the cap cannot hold the smallest block and slab) or
+    returns a plan whose blocks and slabs are tile multiples covering T and V,
+    whose workspace sizes follow their definitions and stay under the cap,
+    and whose slab of W rows stays below 2 GiB."""
+    d = 8 * d8
+    dt = flce.FLCE_BF16 if bf16 else flce.FLCE_F32
+    esz = 2 if bf16 else 4
+    st_, p = flce.flce_plan_status(T, d, V, dt, cap=cap)
+    if st_ == flce.FLCE_ERR_WORKSPACE:
+        assert 0 < cap < 950_000_000
+        return
+    assert st_ == flce.FLCE_OK, flce.last_error()
+    assert p.bwd_ws_bytes <= (cap if cap else 950_000_000)
+    assert p.dz_ws_bytes == p.bwd_block * p.bwd_slab * esz
+    assert p.dh_acc_bytes == (p.bwd_block * d * 4 if p.n_slabs > 1 else 0)
+    assert p.bwd_block % p.tile_t == 0 and p.bwd_slab % p.tile_v == 0
+    assert 0 < p.bwd_block <= 8192
+    if T > 0:
+        assert p.n_blocks * p.bwd_block >= T > (p.n_blocks - 1) * p.bwd_block
+    else:
+        assert p.n_blocks == 0
+    assert p.n_slabs * p.bwd_slab >= V > (p.n_slabs - 1) * p.bwd_slab
+    assert p.bwd_slab * d * esz < 2 ** 31
+    n_vt = -(-V // p.tile_v)
+    assert p.fwd_splits * p.fwd_tiles_per_split >= n_vt > (p.fwd_splits - 1) * p.fwd_tiles_per_split
     assert p.ws_bytes == max(p.fwd_ws_bytes, p.bwd_ws_bytes) + 256
 
 
